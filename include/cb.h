@@ -1,0 +1,215 @@
+/*
+ * cb.h - C ABI of libcb.so: one forward step of ragged continuous-batching attention on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Hugging Face blog "Continuous batching from first principles", sections
+ * "Attention", "KV-cache", "Chunked prefill" and "Continuous batching"; zhangchitc
+ * "continuous-batching", sections "Ragged batching: attention in per-request blocks" and
+ * "Inside the kernel: cu_seqlens splits six rows back into three"):
+ *
+ *   All scheduled requests are packed into one token stream with no batch axis and no
+ *   padding. Request r owns packed rows cu_q_lens[r] .. cu_q_lens[r+1]-1. A decode request
+ *   contributes one row and a prefill chunk contributes q_r rows. Request r has ctx_lens[r]
+ *   tokens cached before the step. Its new tokens sit at positions ctx_lens[r] + i.
+ *   Each query row at position p of request r attends to keys 0..p of request r only. The
+ *   mask is block-diagonal over requests and causal within a request:
+ *       O[t,h,:] = softmax_j( scale * Q[t,h,:] . K_r[j,g,:] ) V_r[j,g,:],   j = 0..p,
+ *   with g = h / (Hq / Hkv). K_r and V_r are the request's keys and values: its cache
+ *   followed by this step's new tokens, which cb_kv_append writes into the cache first.
+ *
+ * Conventions for every call:
+ *   - Pointers are either device pointers (HBM, from hipMalloc or torch) or host pointers.
+ *     Each argument below says which. The library never frees or takes ownership of caller
+ *     memory and never allocates caller-visible device memory.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream). Inputs must stay valid until the work on the stream completes.
+ *   - The return value is 0 (CB_OK) or a negative cb_status. On error nothing has been
+ *     launched. cb_last_error() returns a message for the calling thread.
+ *   - Integer metadata is int32. Float tensors are dense and row-major in the dtype of
+ *     cb_shape.dtype (bf16 or fp32).
+ */
+#ifndef CB_H
+#define CB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CB_OK = 0,
+  CB_ERR_INVALID_ARG = -1,        /* malformed shape, metadata or pointer */
+  CB_ERR_UNSUPPORTED = -2,        /* valid but not implemented (head_dim, group size...) */
+  CB_ERR_HIP = -3,                /* a HIP runtime call failed */
+  CB_ERR_OUT_OF_BLOCKS = -4,      /* the scheduler's free list cannot cover the step */
+  CB_ERR_WORKSPACE_TOO_SMALL = -5,
+  CB_ERR_STATE = -6               /* call out of order (e.g. build twice without commit) */
+} cb_status;
+
+typedef enum { CB_F32 = 0, CB_BF16 = 1 } cb_dtype;
+
+/* Model-side sizes.
+ * num_q_heads % num_kv_heads == 0; head_dim in {64, 128}; block_size == 16.
+ * Hq / Hkv (the query group size G) must be 1, 2, 4, 8 or a multiple of 8.
+ * Paged KV cache, num_blocks physical blocks; for block b and kv head g:
+ *   k_cache[b][g][s][d]  : [num_blocks, Hkv, block_size, head_dim]   (slot-major, as K rows)
+ *   v_cache[b][g][d][s]  : [num_blocks, Hkv, head_dim, block_size]   (V stored transposed)
+ * Both are contiguous, and each (b, g) page is block_size*head_dim elements. Position p of
+ * a request lives in block block_tables[r][p / block_size], slot p % block_size. */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t dtype;                  /* cb_dtype */
+} cb_shape;
+
+/* One ragged step (zhangchitc, "Inside the kernel": cu_seqlens is the prefix sum of the
+ * per-request row counts, e.g. lengths [4,1,1] give [0,4,5,6]).
+ *   cu_q_lens    device int32 [num_reqs+1], nondecreasing, cu[0]=0, cu[R]=num_tokens
+ *   ctx_lens     device int32 [num_reqs], tokens cached before this step (>= 0)
+ *   block_tables device int32 [num_reqs * max_blocks_per_req], row r lists the physical
+ *                blocks of request r in position order; entries past
+ *                ceil((ctx+q)/block_size) are ignored (-1 by convention)
+ *   h_cu_q_lens, h_ctx_lens  host copies of the two arrays above (same values). They are
+ *                used to validate and to plan the launch without a device sync.
+ * A request with zero rows is allowed and produces nothing. */
+typedef struct {
+  int32_t num_reqs;
+  int32_t num_tokens;
+  int32_t max_blocks_per_req;
+  const int32_t* cu_q_lens;
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
+  const int32_t* h_cu_q_lens;
+  const int32_t* h_ctx_lens;
+} cb_batch;
+
+/* ---------------------------------------------------------------------------------------
+ * KV append (zhangchitc "continuous-batching", section "Inside the kernel": the new keys
+ * and values are written into the KV cache, each into its own request's entry, before
+ * attention reads them back).
+ *   k_new, v_new  device [num_tokens, Hkv, head_dim], packed like Q
+ *   k_cache, v_cache  device, layout in cb_shape; updated in place
+ * Row t of request r (position p = ctx_lens[r] + t - cu_q_lens[r]) is copied bit for bit
+ * to k_cache[bt[r][p/bs]][g][p%bs][:] and v_cache[bt[r][p/bs]][g][:][p%bs].
+ * Block ids outside [0, num_blocks) are skipped on the device (no write).
+ * ------------------------------------------------------------------------------------- */
+int cb_kv_append(const cb_shape* shape, const cb_batch* batch, const void* k_new,
+                 const void* v_new, void* k_cache, void* v_cache, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Ragged attention (the operation at the top of this file).
+ *   q        device [num_tokens, Hq, head_dim]
+ *   k_cache, v_cache  device caches, already holding this step's keys/values
+ *   scale    multiplies Q.K before the softmax (the pages show none; 1/sqrt(D) is usual)
+ *   o        device [num_tokens, Hq, head_dim], written in full (dtype of the shape)
+ *   workspace  device scratch of at least cb_ragged_attention_workspace_size() bytes,
+ *            256-byte aligned, owned by the caller. It must not be shared by two calls in
+ *            flight at the same time.
+ * Rows of a request with one row (decode) take a split-K bandwidth path. Rows of a request
+ * with more than one row (prefill chunk) take an MFMA tile path (bf16) or the split-K path
+ * (fp32). Block ids in the tables are not range-checked on the device beyond skipping ids
+ * outside [0, num_blocks); stale or wrong tables give wrong results, never a fault.
+ * ------------------------------------------------------------------------------------- */
+size_t cb_ragged_attention_workspace_size(const cb_shape* shape, const cb_batch* batch);
+
+int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void* q,
+                        const void* k_cache, const void* v_cache, float scale, void* o,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message describing the last error on this thread ("" if none). Owned by the library. */
+const char* cb_last_error(void);
+
+/* Library version string, e.g. "cb 0.1 gfx950". */
+const char* cb_version(void);
+
+/* Tuning knobs (process-wide, host-side). Keys:
+ *   "split_blocks"   KV blocks per split of a decode row; 0 = automatic (default)
+ *   "target_waves"   automatic split sizing aims for at least this many wave items
+ * Returns CB_ERR_INVALID_ARG for an unknown key or a negative value. */
+int cb_set_tuning(const char* key, int32_t value);
+
+/* ---------------------------------------------------------------------------------------
+ * Kernel timing (hipEvents recorded on the stream each kernel is launched on).
+ * cb_profile_enable(1) starts recording a start/stop event pair around every kernel the
+ * library launches. cb_profile_read() waits for the recorded events and returns the summed
+ * duration and the launch count for one kernel id. cb_profile_reset() drops all records.
+ * ------------------------------------------------------------------------------------- */
+enum { CB_KERNEL_APPEND = 0, CB_KERNEL_DECODE = 1, CB_KERNEL_COMBINE = 2, CB_KERNEL_PREFILL = 3,
+       CB_KERNEL_COUNT = 4 };
+int cb_profile_enable(int on);
+int cb_profile_read(int kernel_id, double* total_ms, int64_t* launches);
+int cb_profile_reset(void);
+const char* cb_kernel_name(int kernel_id);
+
+/* ---------------------------------------------------------------------------------------
+ * Host step builder (Hugging Face blog, section "Continuous batching": aim for m tokens per
+ * step, add every decoding request first with one token each, fill the rest with prefill
+ * chunks, remove finished requests at once and admit waiting ones; hassanahmed "How
+ * continuous batching speeds up LLM serving": evict, admit while can_admit, run one step;
+ * the cache lives in fixed-size blocks handed out and reclaimed on demand).
+ *
+ * Host memory only; no HIP calls. Each build():
+ *   1. evicts requests marked done by the previous commit, returning their blocks to the
+ *      tail of the FIFO free list in block-table order;
+ *   2. takes every decode-phase request (admission order, at most m), one token each,
+ *      allocating a block when its position starts a new one;
+ *   3. gives the remaining budget to partly prefilled requests (admission order), each
+ *      taking min(remaining prompt, budget, tokens its blocks plus the free list can hold);
+ *   4. admits waiting requests (FIFO) while budget > 0, the free list holds the blocks of
+ *      the first chunk (min(prompt, budget) tokens), and fewer than max_num_seqs
+ *      requests are running (if max_num_seqs > 0). The first request that does not fit
+ *      stops admission.
+ * A request is done once it has produced out_len tokens (the last prefill chunk produces
+ * the first) or when commit() flags EOS for a step in which it produced a token.
+ * ------------------------------------------------------------------------------------- */
+typedef struct cb_sched cb_sched;
+
+/* The arrays of one built step. They are owned by the scheduler and valid until the next
+ * build/commit/destroy. block_tables is [num_reqs * max_blocks_per_req], -1 padded. */
+typedef struct {
+  int32_t num_reqs;
+  int32_t num_tokens;
+  int32_t max_blocks_per_req;
+  int32_t num_decode;             /* the first num_decode requests are decodes (1 row) */
+  const int64_t* req_ids;         /* [num_reqs] */
+  const int32_t* cu_q_lens;       /* [num_reqs+1] */
+  const int32_t* ctx_lens;        /* [num_reqs] */
+  const int32_t* block_tables;    /* [num_reqs * max_blocks_per_req] */
+  const int32_t* slot_mapping;    /* [num_tokens]: block*block_size + offset of each row */
+  const int32_t* token_to_req;    /* [num_tokens]: index into this step's requests */
+  int32_t num_evicted;
+  int32_t num_admitted;
+  const int64_t* evicted;         /* request ids evicted at the start of this build */
+  const int64_t* admitted;        /* request ids admitted by this build */
+} cb_step;
+
+/* initial_free_list: host int32 [num_blocks], a permutation of 0..num_blocks-1 giving the
+ * allocation order, or NULL for 0,1,2,... Returns NULL on invalid arguments. */
+cb_sched* cb_sched_create(int32_t token_budget, int32_t block_size, int32_t num_blocks,
+                          int32_t max_num_seqs, const int32_t* initial_free_list);
+/* A new request enters the waiting queue. prompt_len >= 1, out_len >= 1. */
+int cb_sched_add(cb_sched* s, int64_t req_id, int32_t prompt_len, int32_t out_len);
+/* A request that is already running with `cached` positions in the cache: either still in
+ * prefill (generated == 0, cached < prompt_len) or decoding (1 <= generated < out_len and
+ * cached == prompt_len + generated - 1). Allocates ceil(cached / block_size) blocks. */
+int cb_sched_add_cached(cb_sched* s, int64_t req_id, int32_t prompt_len, int32_t out_len,
+                        int32_t cached, int32_t generated);
+int cb_sched_build(cb_sched* s, cb_step* out);
+/* eos: host uint8 [num_reqs of the last step] or NULL (finish by out_len only). */
+int cb_sched_commit(cb_sched* s, const uint8_t* eos);
+/* Deep copy (free list, queues and requests); the copy has no step pending. */
+cb_sched* cb_sched_clone(const cb_sched* s);
+void cb_sched_destroy(cb_sched* s);
+int cb_sched_stats(const cb_sched* s, int32_t* num_running, int32_t* num_waiting,
+                   int32_t* num_free_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CB_H */

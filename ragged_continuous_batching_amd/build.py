@@ -1,0 +1,75 @@
+"""Builds libcb.so in-tree with hipcc for gfx950 (runs here without a GPU).
+
+    python -m ragged_continuous_batching_amd.build [-j N]
+
+Every HIP translation unit is compiled with packed-fp32 instruction selection disabled
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the hand-written kernels use no
+packed fp32 arithmetic either. Host-only sources (``*.cpp``) are compiled as C++.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libcb.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    return os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def common_flags():
+    return ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def compile_one(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if src.endswith(".hip"):
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-x", "hip", "-c", src, "-o", obj, *common_flags(),
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    else:
+        rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+        cmd = [hipcc(), "-x", "c++", "-c", src, "-o", obj, *common_flags(), f"-I{rocm}/include",
+               "-D__HIP_PLATFORM_AMD__=1"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} from {len(srcs)} sources")
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-j", type=int, default=min(8, os.cpu_count() or 1))
+    args = ap.parse_args(argv)
+    build(args.j, verbose=True)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,385 @@
+// C ABI entry points: argument validation, the launch planner, the plan upload, kernel
+// launches and kernel timing. Host code only; the kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cb.h"
+#include "cb_common.h"
+#include "cb_plan.h"
+
+namespace cb {
+
+std::string& last_error() {
+  thread_local std::string msg;
+  return msg;
+}
+
+hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int head_dim, hipStream_t s);
+hipError_t launch_rows(const RowArgs& a, int elem_bytes, int head_dim, int group, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// ---- tuning -----------------------------------------------------------------------------
+struct Tuning {
+  int32_t split_blocks = 0;       // 0 = automatic
+  int32_t target_waves = 16384;
+};
+Tuning g_tuning;
+
+// ---- kernel timing ----------------------------------------------------------------------
+struct ProfRec {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+struct ProfScope {
+  int kernel;
+  hipStream_t stream;
+  hipEvent_t start = nullptr, stop = nullptr;
+  ProfScope(int k, hipStream_t s) : kernel(k), stream(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) {
+      start = stop = nullptr;
+      return;
+    }
+    hipEventRecord(start, stream);
+  }
+  ~ProfScope() {
+    if (!start) return;
+    hipEventRecord(stop, stream);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({kernel, start, stop});
+  }
+};
+
+// ---- pinned staging ring for the plan upload -------------------------------------------
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool in_flight = false;
+};
+constexpr int kRing = 8;
+std::mutex g_ring_mu;
+Staging g_ring[kRing];
+int g_ring_next = 0;
+
+// Copies `bytes` from `src` to device `dst` on `stream` through pinned memory. The staging
+// slot is reused only after its previous copy has completed (event wait).
+int upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return CB_OK;
+  std::lock_guard<std::mutex> lk(g_ring_mu);
+  Staging& s = g_ring[g_ring_next];
+  g_ring_next = (g_ring_next + 1) % kRing;
+  if (s.in_flight) {
+    if (hipEventSynchronize(s.ev) != hipSuccess) return fail(CB_ERR_HIP, "plan upload: event wait failed");
+    s.in_flight = false;
+  }
+  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
+    return fail(CB_ERR_HIP, "plan upload: hipEventCreate failed");
+  if (s.cap < bytes) {
+    if (s.host) hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    size_t cap = std::max<size_t>(bytes, 1 << 16);
+    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess)
+      return fail(CB_ERR_HIP, "plan upload: hipHostMalloc(%zu) failed", cap);
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src, bytes);
+  hipError_t e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
+  if (hipEventRecord(s.ev, stream) != hipSuccess) return fail(CB_ERR_HIP, "plan upload: event record failed");
+  s.in_flight = true;
+  return CB_OK;
+}
+
+// ---- validation -------------------------------------------------------------------------
+inline int elem_bytes(const cb_shape* s) { return s->dtype == CB_BF16 ? 2 : 4; }
+inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const cb_shape* s) {
+  if (!s) return fail(CB_ERR_INVALID_ARG, "shape is NULL");
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return fail(CB_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  const int g = s->num_q_heads / s->num_kv_heads;
+  if (!(g == 1 || g == 2 || g == 4 || g % 8 == 0))
+    return fail(CB_ERR_UNSUPPORTED, "query group size %d not supported (1, 2, 4 or a multiple of 8)", g);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(CB_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", s->head_dim);
+  if (s->block_size != kBlockSize) return fail(CB_ERR_UNSUPPORTED, "block_size must be %d", kBlockSize);
+  if (s->num_blocks < 1) return fail(CB_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (s->dtype != CB_F32 && s->dtype != CB_BF16) return fail(CB_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
+  return CB_OK;
+}
+
+int check_batch(const cb_shape* s, const cb_batch* b) {
+  if (!b) return fail(CB_ERR_INVALID_ARG, "batch is NULL");
+  if (b->num_reqs < 0 || b->num_tokens < 0 || b->max_blocks_per_req < 0)
+    return fail(CB_ERR_INVALID_ARG, "negative count in batch");
+  if (b->num_reqs == 0) {
+    if (b->num_tokens != 0) return fail(CB_ERR_INVALID_ARG, "num_tokens > 0 with no requests");
+    return CB_OK;
+  }
+  if (!b->h_cu_q_lens || !b->h_ctx_lens) return fail(CB_ERR_INVALID_ARG, "host mirrors are required");
+  if (!b->cu_q_lens || !b->ctx_lens || !b->block_tables)
+    return fail(CB_ERR_INVALID_ARG, "device metadata pointer is NULL");
+  if (b->h_cu_q_lens[0] != 0) return fail(CB_ERR_INVALID_ARG, "cu_q_lens[0] must be 0");
+  for (int32_t r = 0; r < b->num_reqs; ++r) {
+    const int32_t q = b->h_cu_q_lens[r + 1] - b->h_cu_q_lens[r];
+    const int32_t c = b->h_ctx_lens[r];
+    if (q < 0) return fail(CB_ERR_INVALID_ARG, "cu_q_lens decreases at request %d", r);
+    if (c < 0) return fail(CB_ERR_INVALID_ARG, "ctx_lens[%d] = %d is negative", r, c);
+    if (q > 0 && ceil_div(static_cast<int64_t>(c) + q, s->block_size) > b->max_blocks_per_req)
+      return fail(CB_ERR_INVALID_ARG, "request %d needs %d blocks but max_blocks_per_req is %d", r,
+                  ceil_div(static_cast<int64_t>(c) + q, s->block_size), b->max_blocks_per_req);
+    if (static_cast<int64_t>(c) + q > (int64_t{1} << 30)) return fail(CB_ERR_INVALID_ARG, "request %d too long", r);
+  }
+  if (b->h_cu_q_lens[b->num_reqs] != b->num_tokens)
+    return fail(CB_ERR_INVALID_ARG, "cu_q_lens[num_reqs] = %d but num_tokens = %d", b->h_cu_q_lens[b->num_reqs],
+                b->num_tokens);
+  return CB_OK;
+}
+
+// ---- the launch plan ----------------------------------------------------------------------
+inline size_t align256(size_t x) { return (x + 255) & ~size_t{255}; }
+
+struct Plan {
+  std::vector<RowSplit> splits;
+  std::vector<CombineRow> combine;
+  std::vector<PrefillItem> prefill;
+  int32_t n_parts = 0;
+  int group = 1;         // query heads per decode wave
+  int n_sub = 1;         // decode waves per kv head
+  size_t off_combine = 0, off_prefill = 0, plan_bytes = 0, off_part_o = 0, off_part_ml = 0, total = 0;
+};
+
+void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
+  const int q_per_kv = s->num_q_heads / s->num_kv_heads;
+  p.group = q_per_kv >= 8 ? 8 : q_per_kv;
+  p.n_sub = q_per_kv / p.group;
+  const bool mfma_prefill = s->dtype == CB_BF16;
+
+  // rows that take the split-K path, longest first
+  struct Row { int32_t token, req, kv_len; };
+  std::vector<Row> rows;
+  int64_t total_blocks = 0;
+  for (int32_t r = 0; r < b->num_reqs; ++r) {
+    const int32_t t0 = b->h_cu_q_lens[r], q = b->h_cu_q_lens[r + 1] - t0, c = b->h_ctx_lens[r];
+    if (q == 0) continue;
+    if (q == 1 || !mfma_prefill) {
+      for (int32_t i = 0; i < q; ++i) {
+        rows.push_back({t0 + i, r, c + i + 1});
+        total_blocks += ceil_div(c + i + 1, kBlockSize);
+      }
+    } else {
+      const int32_t n_qt = ceil_div(q, kPrefillRows);
+      for (int32_t qt = 0; qt < n_qt; ++qt) {
+        const int32_t qb = qt * kPrefillRows;
+        const int32_t keys = c + std::min(qb + kPrefillRows, q);
+        const int32_t tiles = ceil_div(keys, kPrefillKeys);
+        for (int32_t h = 0; h < s->num_q_heads; ++h) p.prefill.push_back({r, qb, h, tiles});
+      }
+    }
+  }
+  std::stable_sort(p.prefill.begin(), p.prefill.end(),
+                   [](const PrefillItem& x, const PrefillItem& y) { return x.kv_tiles > y.kv_tiles; });
+  std::stable_sort(rows.begin(), rows.end(), [](const Row& x, const Row& y) { return x.kv_len > y.kv_len; });
+
+  int32_t split = g_tuning.split_blocks;
+  if (split <= 0) {
+    const int64_t units = total_blocks * s->num_kv_heads * p.n_sub;
+    const int64_t target = std::max<int32_t>(g_tuning.target_waves, 1);
+    split = static_cast<int32_t>(std::clamp<int64_t>((units + target - 1) / target, 4, 64));
+  }
+  for (const Row& row : rows) {
+    const int32_t nb = ceil_div(row.kv_len, kBlockSize);
+    const int32_t ns = ceil_div(nb, split);
+    if (ns == 1) {
+      p.splits.push_back({row.token, row.req, 0, nb, row.kv_len, -1});
+      continue;
+    }
+    p.combine.push_back({row.token, p.n_parts, ns, 0});
+    for (int32_t k = 0; k < ns; ++k)
+      p.splits.push_back({row.token, row.req, k * split, std::min(nb, (k + 1) * split), row.kv_len, p.n_parts + k});
+    p.n_parts += ns;
+  }
+
+  const size_t eb = 4;
+  p.off_combine = align256(p.splits.size() * sizeof(RowSplit));
+  p.off_prefill = p.off_combine + align256(p.combine.size() * sizeof(CombineRow));
+  p.plan_bytes = p.off_prefill + p.prefill.size() * sizeof(PrefillItem);
+  p.off_part_o = align256(p.plan_bytes);
+  p.off_part_ml = p.off_part_o + align256(static_cast<size_t>(p.n_parts) * s->num_q_heads * s->head_dim * eb);
+  p.total = p.off_part_ml + align256(static_cast<size_t>(p.n_parts) * s->num_q_heads * 2 * eb);
+}
+
+}  // namespace
+}  // namespace cb
+
+using namespace cb;
+
+extern "C" const char* cb_last_error(void) { return last_error().c_str(); }
+
+extern "C" const char* cb_version(void) { return "cb 0.1 gfx950"; }
+
+extern "C" int cb_set_tuning(const char* key, int32_t value) {
+  if (!key || value < 0) return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: bad key or value");
+  if (std::strcmp(key, "split_blocks") == 0) {
+    g_tuning.split_blocks = value;
+  } else if (std::strcmp(key, "target_waves") == 0) {
+    g_tuning.target_waves = value;
+  } else {
+    return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: unknown key '%s'", key);
+  }
+  return CB_OK;
+}
+
+extern "C" const char* cb_kernel_name(int k) {
+  switch (k) {
+    case CB_KERNEL_APPEND: return "kv_append_kernel";
+    case CB_KERNEL_DECODE: return "row_attn_kernel";
+    case CB_KERNEL_COMBINE: return "combine_kernel";
+    case CB_KERNEL_PREFILL: return "prefill_kernel";
+    default: return "";
+  }
+}
+
+extern "C" int cb_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return CB_OK;
+}
+
+extern "C" int cb_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    hipEventSynchronize(r.stop);
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  return CB_OK;
+}
+
+extern "C" int cb_profile_read(int kernel_id, double* total_ms, int64_t* launches) {
+  if (kernel_id < 0 || kernel_id >= CB_KERNEL_COUNT) return fail(CB_ERR_INVALID_ARG, "bad kernel id %d", kernel_id);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double sum = 0;
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (r.kernel != kernel_id) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return fail(CB_ERR_HIP, "cb_profile_read: event wait failed");
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      return fail(CB_ERR_HIP, "cb_profile_read: elapsed time failed");
+    sum += ms;
+    ++n;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = n;
+  return CB_OK;
+}
+
+extern "C" int cb_kv_append(const cb_shape* shape, const cb_batch* batch, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_batch(shape, batch))) return st;
+  if (batch->num_tokens == 0) return CB_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache) return fail(CB_ERR_INVALID_ARG, "cb_kv_append: NULL tensor");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(CB_ERR_INVALID_ARG, "cb_kv_append: tensors must be 16-byte aligned");
+  AppendArgs a{k_new, v_new, k_cache, v_cache, batch->cu_q_lens, batch->ctx_lens, batch->block_tables,
+               batch->num_reqs, batch->num_tokens, batch->max_blocks_per_req, shape->num_kv_heads, shape->num_blocks};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    ProfScope ps(CB_KERNEL_APPEND, s);
+    e = launch_kv_append(a, elem_bytes(shape), shape->head_dim, s);
+  }
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_kv_append: launch failed: %s", hipGetErrorString(e));
+  return CB_OK;
+}
+
+extern "C" size_t cb_ragged_attention_workspace_size(const cb_shape* shape, const cb_batch* batch) {
+  if (check_shape(shape) || check_batch(shape, batch)) return 0;
+  if (batch->num_tokens == 0) return 0;
+  Plan p;
+  make_plan(shape, batch, p);
+  return p.total;
+}
+
+extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void* q,
+                                   const void* k_cache, const void* v_cache, float scale, void* o,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_batch(shape, batch))) return st;
+  if (batch->num_tokens == 0) return CB_OK;
+  if (!q || !k_cache || !v_cache || !o) return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: NULL tensor");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: tensors must be 16-byte aligned");
+  Plan p;
+  make_plan(shape, batch, p);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(CB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, p.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(CB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  std::vector<char> host(p.plan_bytes);
+  if (!p.splits.empty()) std::memcpy(host.data(), p.splits.data(), p.splits.size() * sizeof(RowSplit));
+  if (!p.combine.empty())
+    std::memcpy(host.data() + p.off_combine, p.combine.data(), p.combine.size() * sizeof(CombineRow));
+  if (!p.prefill.empty())
+    std::memcpy(host.data() + p.off_prefill, p.prefill.data(), p.prefill.size() * sizeof(PrefillItem));
+  if ((st = upload(ws, host.data(), p.plan_bytes, s))) return st;
+
+  const int eb = elem_bytes(shape);
+  const float scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  hipError_t e = hipSuccess;
+  if (!p.prefill.empty()) {
+    PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
+                   batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
+                   shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2};
+    ProfScope ps(CB_KERNEL_PREFILL, s);
+    e = launch_prefill(pa, shape->head_dim, s);
+  }
+  if (e == hipSuccess && !p.splits.empty()) {
+    RowArgs ra{q, k_cache, v_cache, o,
+               reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml),
+               reinterpret_cast<const RowSplit*>(ws), batch->block_tables,
+               static_cast<int32_t>(p.splits.size()) * shape->num_kv_heads * p.n_sub,
+               shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2};
+    ProfScope ps(CB_KERNEL_DECODE, s);
+    e = launch_rows(ra, eb, shape->head_dim, p.group, s);
+  }
+  if (e == hipSuccess && !p.combine.empty()) {
+    CombineArgs ca{o, reinterpret_cast<const float*>(ws + p.off_part_o),
+                   reinterpret_cast<const float*>(ws + p.off_part_ml),
+                   reinterpret_cast<const CombineRow*>(ws + p.off_combine), static_cast<int32_t>(p.combine.size()),
+                   shape->num_q_heads};
+    ProfScope ps(CB_KERNEL_COMBINE, s);
+    e = launch_combine(ca, eb, shape->head_dim, s);
+  }
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_ragged_attention: launch failed: %s", hipGetErrorString(e));
+  return CB_OK;
+}

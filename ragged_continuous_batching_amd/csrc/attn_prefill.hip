@@ -1,0 +1,252 @@
+// Prefill-chunk attention with bf16 MFMA tiles and an fp32 online softmax.
+//
+// Hugging Face blog "Continuous batching from first principles": scores cost O(n^2 d)
+// (section "Attention"); a chunk attends to the cached keys of its own request plus its own
+// keys, with the causal mask cut "in the middle" (section "Chunked prefill"); requests
+// never see each other (section "Continuous batching"). zhangchitc "continuous-batching":
+// masked pairs are not computed at all, and the cache is read one block at a time into a
+// running online-softmax state.
+//
+// One work-group (4 waves) = 128 query rows of one request and one query head. Each wave
+// owns 32 rows. Keys stream through LDS in tiles of 64 (4 cache blocks), double-buffered:
+// one barrier per tile, and the next tile's global loads overlap the current tile's math.
+// The products are computed transposed so that the query index stays the lane index:
+//   S^T[key][q] = K Q^T      A = K tile rows from LDS, B = the wave's Q rows (registers)
+//   O^T[d][q]  += V^T P^T    A = V^T rows from LDS (the cache stores V transposed),
+//                            B = P^T, which is exactly the S^T accumulator layout
+// with v_mfma_f32_32x32x16_bf16. Each lane owns one query column, so the row max, the
+// rescale factor and the row sum are per-lane values. Only the two lane halves (keys split
+// across lanes l and l^32) exchange the max. Within a 16-key MFMA step the key order is
+// permuted identically for A and B, so that P needs no shuffles. Tiles that lie past every
+// row of a wave are skipped, and the causal mask is only evaluated on tiles that cross the
+// diagonal.
+#include "cb_device.h"
+
+namespace cb {
+
+template <int D>
+struct PrefillGeom {
+  static constexpr int KS = D + 8;                    // K tile row stride (elements)
+  static constexpr int VS = kPrefillKeys + 4;         // V^T tile row stride (elements)
+  static constexpr int K_TILE = kPrefillKeys * KS;
+  static constexpr int V_TILE = D * VS;
+  static constexpr int LDS_ELEMS = 2 * (K_TILE + V_TILE);
+  static constexpr int KCH = kPrefillKeys * D / 8 / 256;   // 16-byte K chunks per thread
+  static constexpr int VCH = D * kPrefillKeys / 8 / 256;   // 16-byte V chunks per thread
+  static constexpr int DCH = D / 16;                  // MFMA k-steps over the head dim
+  static constexpr int DT = D / 32;                   // 32-wide output tiles over the head dim
+};
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using Geo = PrefillGeom<D>;
+  constexpr int KS = Geo::KS, VS = Geo::VS, KCH = Geo::KCH, VCH = Geo::VCH, DCH = Geo::DCH, DT = Geo::DT;
+  __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
+
+  const PrefillItem it = a.items[blockIdx.x];
+  const int r = it.req, h = it.head;
+  const int hkv = a.num_kv_heads;
+  const int g = h / (a.num_q_heads / hkv);
+  const int t0 = a.cu_q_lens[r];
+  const int nq = a.cu_q_lens[r + 1] - t0;
+  const int c = a.ctx_lens[r];
+  const int kv_len = c + nq;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = wave_id();
+  const int col = lane & 31, grp = lane >> 5;
+  const int wave_row0 = it.q_begin + wave * 32;              // first row of this wave
+  const int qrow = wave_row0 + col;                           // this lane's row in the request
+  const bool wave_active = wave_row0 < nq;
+  const int wave_keys = c + min(wave_row0 + 31, nq - 1) + 1;  // keys any row of the wave sees
+  const int wg_keys = c + min(it.q_begin + kPrefillRows - 1, nq - 1) + 1;
+  const int n_tiles = (wg_keys + kPrefillKeys - 1) / kPrefillKeys;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
+  const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+
+  // the wave's query rows as the B operand of K Q^T: Q[qrow][16*dc + 8*grp .. +8]
+  bf16x8 qf[DCH];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(t0 + qrow) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int dc = 0; dc < DCH; ++dc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow < nq) v = *reinterpret_cast<const u32x4*>(qp + dc * 16 + grp * 8);
+      qf[dc] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // global -> registers for key tile j (zeros for positions >= kv_len)
+  u32x4 kreg[KCH], vreg[VCH];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int cid = tid + 256 * u;
+      const int key = cid / (D / 8), dc = cid % (D / 8);
+      const int pos = j * kPrefillKeys + key;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (pos < kv_len) {
+        int blk = bt[pos / kBlockSize];
+        if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = 0;
+        v = *reinterpret_cast<const u32x4*>(kc + (static_cast<int64_t>(blk) * hkv + g) * page_elems +
+                                            (pos % kBlockSize) * D + dc * 8);
+      }
+      kreg[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int cid = tid + 256 * u;
+      const int d = cid / 8, kq = cid % 8;                      // key octet kq of the tile
+      const int pos = j * kPrefillKeys + kq * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (pos < kv_len) {
+        int blk = bt[pos / kBlockSize];
+        if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = 0;
+        v = *reinterpret_cast<const u32x4*>(vc + (static_cast<int64_t>(blk) * hkv + g) * page_elems +
+                                            d * kBlockSize + (pos % kBlockSize));
+        if (pos + 8 > kv_len) {             // the octet straddles the end: clear stale slots
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int p0 = pos + 2 * w;
+            uint32_t keep = (p0 < kv_len ? 0x0000ffffu : 0u) | (p0 + 1 < kv_len ? 0xffff0000u : 0u);
+            v[w] &= keep;
+          }
+        }
+      }
+      vreg[u] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* kl = lds + buf * Geo::K_TILE;
+    uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int cid = tid + 256 * u;
+      const int key = cid / (D / 8), dc = cid % (D / 8);
+      *reinterpret_cast<u32x4*>(kl + key * KS + dc * 8) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int cid = tid + 256 * u;
+      const int d = cid / 8, kq = cid % 8;
+      u32x2* dst = reinterpret_cast<u32x2*>(vl + d * VS + kq * 8);
+      dst[0] = u32x2{vreg[u][0], vreg[u][1]};
+      dst[1] = u32x2{vreg[u][2], vreg[u][3]};
+    }
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int qpos = c + qrow;
+
+  load_tile(0);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (!wave_active || j * kPrefillKeys >= wave_keys) continue;
+
+    const uint16_t* kl = lds + buf * Geo::K_TILE;
+    const uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
+    // S^T for keys [64j, 64j+32) and [64j+32, 64j+64)
+    f32x16 st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < DCH; ++dc) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + col) * KS + dc * 16 + grp * 8);
+        st[kt] = mfma32(ka, qf[dc], st[kt]);
+      }
+    }
+    // scale, causal mask on diagonal tiles, online softmax (this lane's query = column)
+    const bool diag = j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = st[kt][i] * a.scale_log2;
+        if (diag) {
+          const int kpos = j * kPrefillKeys + kt * 32 + (i >> 2) * 8 + grp * 4 + (i & 3);
+          s = kpos <= qpos ? s : -INFINITY;
+        }
+        st[kt][i] = s;
+        mx = fmaxf(mx, s);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(st[kt][half * 8 + 2 * e] - m_new);
+          const float p1 = __builtin_amdgcn_exp2f(st[kt][half * 8 + 2 * e + 1] - m_new);
+          psum += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* vrow = vl + (dt * 32 + col) * VS + grp * 4;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 16);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 8);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        oacc[dt] = mfma32(va, pb[ks], oacc[dt]);
+      }
+    }
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow >= nq) return;
+  const float inv = 1.f / l_tot;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + (static_cast<int64_t>(t0 + qrow) * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = dt * 32 + q4 * 8 + grp * 4;
+      const uint32_t w0 = pack_bf16x2(oacc[dt][q4 * 4 + 0] * inv, oacc[dt][q4 * 4 + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(oacc[dt][q4 * 4 + 2] * inv, oacc[dt][q4 * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + d) = u32x2{w0, w1};
+    }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s) {
+  if (a.n_items == 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3(a.n_items), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3(a.n_items), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace cb

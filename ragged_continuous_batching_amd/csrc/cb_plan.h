@@ -1,0 +1,91 @@
+// Work descriptors that the host planner writes into the workspace and the kernels read.
+// Plain structs of int32 so that host and device agree on the layout byte for byte.
+#pragma once
+
+#include <cstdint>
+
+namespace cb {
+
+// One split of one single-row attention (a decode row, or any row of an fp32 prefill):
+// keys [blk_begin*bs, min(blk_end*bs, kv_len)) of request `req`, for packed row `token`.
+// part < 0: the row has one split and the kernel writes O directly; otherwise the split's
+// unnormalised output and (max, sum) go to partial slot `part` and a combine pass merges.
+struct RowSplit {
+  int32_t token;
+  int32_t req;
+  int32_t blk_begin;
+  int32_t blk_end;
+  int32_t kv_len;
+  int32_t part;
+};
+
+// A row with more than one split: partial slots part_begin .. part_begin+n_parts-1.
+struct CombineRow {
+  int32_t token;
+  int32_t part_begin;
+  int32_t n_parts;
+  int32_t pad;
+};
+
+// One tile of a prefill chunk: rows q_begin .. q_begin+kPrefillRows-1 of request `req`
+// (clipped to its row count), query head `head`.
+struct PrefillItem {
+  int32_t req;
+  int32_t q_begin;
+  int32_t head;
+  int32_t kv_tiles;     // key tiles this item walks (used for ordering; kept for tracing)
+};
+
+constexpr int kBlockSize = 16;         // KV positions per physical block
+constexpr int kPrefillRows = 128;      // query rows per prefill work-group (4 waves x 32)
+constexpr int kPrefillKeys = 64;       // keys per prefill K/V tile (4 blocks)
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* cu_q_lens;
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
+  int32_t num_reqs, num_tokens, max_blocks, num_kv_heads, num_blocks;
+};
+
+struct RowArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* o;
+  float* part_o;          // [n_parts, Hq, D] fp32
+  float* part_ml;         // [n_parts, Hq, 2] fp32: running max (log2 units), sum
+  const RowSplit* splits;
+  const int32_t* block_tables;
+  int32_t n_items;        // splits * num_kv_heads
+  int32_t num_q_heads, num_kv_heads, max_blocks, num_blocks;
+  float scale_log2;       // scale * log2(e)
+};
+
+struct CombineArgs {
+  void* o;
+  const float* part_o;
+  const float* part_ml;
+  const CombineRow* rows;
+  int32_t n_rows;
+  int32_t num_q_heads;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* o;
+  const PrefillItem* items;
+  const int32_t* cu_q_lens;
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
+  int32_t n_items;
+  int32_t num_q_heads, num_kv_heads, max_blocks, num_blocks;
+  float scale_log2;
+};
+
+}  // namespace cb

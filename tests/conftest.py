@@ -25,3 +25,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    """Name each GPU test on stdout before it touches the device (flushed), so that a run
+    that ends abruptly still says which case was running."""
+    if "gpu" in request.keywords:
+        print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield

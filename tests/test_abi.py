@@ -1,0 +1,135 @@
+"""The C-ABI library (CPU only): it loads, exports every function that include/cb.h declares,
+and rejects malformed arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from ragged_continuous_batching_amd import cb
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cb.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cb_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(cb.lib, n), f"{n} declared in cb.h but not exported"
+    assert set(names) == set(cb.EXPORTED)
+
+
+def test_version_and_names():
+    assert "gfx950" in cb.cb_version()
+    assert cb.cb_kernel_name(cb.CB_KERNEL_DECODE) == "row_attn_kernel"
+    assert cb.cb_kernel_name(99) == ""
+
+
+def _shape(**kw):
+    d = dict(num_q_heads=4, num_kv_heads=2, head_dim=128, num_blocks=16, dtype="bf16")
+    d.update(kw)
+    return cb.make_shape(**d)
+
+
+def _batch(cu, ctx, maxb):
+    """cb_batch with host mirrors only; device pointers are dummies that are never read."""
+    cu = np.asarray(cu, np.int32)
+    ctx = np.asarray(ctx, np.int32)
+    b = cb.cb_batch(len(ctx), int(cu[-1]), maxb, 256, 256, 256, cu.ctypes.data, ctx.ctypes.data)
+    b._keep = (cu, ctx)
+    return b
+
+
+FAKE = 1 << 20   # 16-byte aligned non-null address; validation fails before any use
+
+
+@pytest.mark.parametrize("shape_kw,status", [
+    (dict(num_q_heads=6, num_kv_heads=4), cb.CB_ERR_INVALID_ARG),
+    (dict(num_q_heads=12, num_kv_heads=4), cb.CB_ERR_UNSUPPORTED),     # group of 3
+    (dict(head_dim=96), cb.CB_ERR_UNSUPPORTED),
+    (dict(block_size=8), cb.CB_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), cb.CB_ERR_INVALID_ARG),
+])
+def test_bad_shape_rejected(shape_kw, status):
+    shape = _shape(**shape_kw)
+    b = _batch([0, 1], [3], 1)
+    rc = cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, 1.0, FAKE, FAKE,
+                                    1 << 20, None)
+    assert rc == status, cb.cb_last_error()
+    assert cb.cb_last_error()
+
+
+@pytest.mark.parametrize("cu,ctx,maxb,why", [
+    ([1, 2], [0], 4, "cu_q_lens[0]"),
+    ([0, 3, 2], [0, 0], 4, "decreases"),
+    ([0, 2], [-1], 4, "negative"),
+    ([0, 2], [31], 1, "needs 3 blocks"),
+])
+def test_bad_metadata_rejected(cu, ctx, maxb, why):
+    shape = _shape()
+    b = _batch(cu, ctx, maxb)
+    for rc in (
+        cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, 1 << 30,
+                                   None),
+        cb.lib.cb_kv_append(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None),
+    ):
+        assert rc == cb.CB_ERR_INVALID_ARG
+        assert why in cb.cb_last_error()
+    assert cb.cb_ragged_attention_workspace_size(shape, b) == 0
+
+
+def test_num_tokens_mismatch_and_alignment():
+    shape = _shape()
+    b = _batch([0, 2], [0], 1)
+    b.num_tokens = 3
+    assert cb.lib.cb_kv_append(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None) == cb.CB_ERR_INVALID_ARG
+    b = _batch([0, 2], [0], 1)
+    rc = cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE + 2, FAKE, FAKE, 1.0, FAKE, FAKE,
+                                    1 << 30, None)
+    assert rc == cb.CB_ERR_INVALID_ARG and "aligned" in cb.cb_last_error()
+
+
+def test_workspace_checks():
+    shape = _shape()
+    b = _batch([0, 1, 2], [4000, 17], 256)
+    need = cb.cb_ragged_attention_workspace_size(shape, b)
+    assert need > 0
+    rc = cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, need - 1,
+                                    None)
+    assert rc == cb.CB_ERR_WORKSPACE_TOO_SMALL
+    rc = cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, 1.0, FAKE, FAKE + 16,
+                                    need, None)
+    assert rc == cb.CB_ERR_INVALID_ARG and "256-byte" in cb.cb_last_error()
+
+
+def test_empty_batch_is_a_no_op():
+    shape = _shape()
+    cu = np.zeros(1, np.int32)
+    b = cb.cb_batch(0, 0, 0, None, None, None, cu.ctypes.data, cu.ctypes.data)
+    assert cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), None, None, None, 1.0, None, None, 0,
+                                      None) == 0
+    assert cb.lib.cb_kv_append(ctypes.byref(shape), ctypes.byref(b), None, None, None, None, None) == 0
+    assert cb.cb_ragged_attention_workspace_size(shape, b) == 0
+
+
+def test_tuning_keys():
+    cb.cb_set_tuning("split_blocks", 0)
+    with pytest.raises(cb.CbError):
+        cb.cb_set_tuning("no_such_key", 1)
+    with pytest.raises(cb.CbError):
+        cb.cb_set_tuning("split_blocks", -1)
+
+
+def test_kv_bytes_per_position_matches_pages():
+    """Hugging Face blog, "KV-cache": one Llama-2-7B position of one layer = 8,192 values =
+    16 KB in fp16. The two cache pages of a block hold exactly that per position."""
+    shape = cb.make_shape(32, 32, 128, 1, "bf16")
+    per_block_bytes = 2 * shape.num_kv_heads * shape.block_size * shape.head_dim * 2
+    assert per_block_bytes // shape.block_size == 16384

@@ -1,0 +1,107 @@
+"""The C++ step builder (cb_sched_*) against the Python reference, bit for bit (CPU only)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle.scheduler import OutOfBlocks, RefScheduler
+from ragged_continuous_batching_amd import cb
+
+
+def pair(wl: W.Workload):
+    ref = RefScheduler(wl.token_budget, wl.block_size, wl.num_blocks, wl.max_num_seqs, wl.free_list)
+    lib = cb.Scheduler(wl.token_budget, wl.block_size, wl.num_blocks, wl.max_num_seqs, wl.free_list)
+    for r in wl.requests:
+        if r.cached is None:
+            ref.add(r.req_id, r.prompt_len, r.out_len)
+            lib.add(r.req_id, r.prompt_len, r.out_len)
+        else:
+            ref.add_cached(r.req_id, r.prompt_len, r.out_len, r.cached, r.generated)
+            lib.add_cached(r.req_id, r.prompt_len, r.out_len, r.cached, r.generated)
+    return ref, lib
+
+
+def same_step(a, b):
+    assert a.num_decode == b.num_decode
+    assert a.evicted == b.evicted and a.admitted == b.admitted
+    for name in ("req_ids", "cu_q_lens", "ctx_lens", "slot_mapping", "token_to_req"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    assert a.block_tables.shape == b.block_tables.shape
+    assert np.array_equal(a.block_tables, b.block_tables)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_static_configs(cid):
+    ref, lib = pair(W.config(cid))
+    same_step(ref.build(), lib.build())
+
+
+def run_trace(wl, steps, eos_rate=0.0, seed=0):
+    ref, lib = pair(wl)
+    rng = np.random.default_rng(seed)
+    for k in range(steps):
+        for r in wl.arrivals[k]:
+            ref.add(r.req_id, r.prompt_len, r.out_len)
+            lib.add(r.req_id, r.prompt_len, r.out_len)
+        a, b = ref.build(), lib.build()
+        same_step(a, b)
+        eos = (rng.random(a.num_reqs) < eos_rate).astype(np.uint8) if eos_rate else None
+        ref.commit(eos)
+        lib.commit(eos)
+        assert lib.stats() == (len(ref.running), len(ref.waiting), ref.num_free_blocks)
+
+
+def test_trace_config5_all_steps():
+    run_trace(W.config(5), 500)
+
+
+def test_trace_small_with_eos_and_block_pressure():
+    wl = W.trace_workload(seed=21, steps=400, rate=1.5, prompt_median=30, prompt_max=200, out_mean=20,
+                          token_budget=64, num_blocks=90)
+    run_trace(wl, 400, eos_rate=0.05, seed=3)
+
+
+def test_max_num_seqs_parity():
+    wl = W.trace_workload(seed=22, steps=200, rate=3, prompt_median=20, prompt_max=100, out_mean=10,
+                          token_budget=48, num_blocks=400)
+    wl.max_num_seqs = 5
+    run_trace(wl, 200)
+
+
+def test_errors_match_reference():
+    ref = RefScheduler(64, 4, 1)
+    lib = cb.Scheduler(64, 4, 1)
+    ref.add_cached(0, 4, 5, 4, 1)
+    lib.add_cached(0, 4, 5, 4, 1)
+    with pytest.raises(OutOfBlocks):
+        ref.build()
+    with pytest.raises(cb.CbError) as e:
+        lib.build()
+    assert e.value.status == cb.CB_ERR_OUT_OF_BLOCKS
+
+
+def test_state_errors():
+    s = cb.Scheduler(8, 16, 4)
+    with pytest.raises(cb.CbError) as e:
+        s.commit()
+    assert e.value.status == cb.CB_ERR_STATE
+    s.add(0, 3, 2)
+    s.build()
+    with pytest.raises(cb.CbError) as e:
+        s.build()
+    assert e.value.status == cb.CB_ERR_STATE
+    with pytest.raises(cb.CbError):
+        s.add_cached(1, 4, 4, 9, 0)                     # inconsistent state
+    with pytest.raises(cb.CbError):
+        cb.Scheduler(8, 16, 3, free_list=[0, 0, 1])       # not a permutation
+
+
+def test_clone_replays_the_same_step():
+    wl = W.config(2)
+    _, lib = pair(wl)
+    c1, c2 = lib.clone(), lib.clone()
+    a, b = c1.build(), c2.build()
+    same_step(a, b)
+    c1.commit()
+    nxt = c1.build()                                   # the clone advances on its own
+    assert np.array_equal(nxt.ctx_lens[:64], a.ctx_lens[:64] + 1)
+    same_step(lib.build(), b)                          # the original is untouched
