@@ -1,0 +1,239 @@
+"""Benchmark: one step of the ragged continuous-batching hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+A step is the whole path over one batch: host batch build (a fresh copy of the scheduler
+state, decode first, chunks up to m, block allocation), the metadata upload, cb_kv_append,
+cb_ragged_attention (prefill MFMA tiles, split-K decode, combine), and the commit. Inputs
+(Q, new K/V, the cached history) are resident in HBM before timing starts. The default
+workload is the Llama-2-7B-shaped mixed step: Hq = Hkv = 32, D = 128, bf16, m = 2048,
+64 decodes with contexts U{512..4096} plus two 992-token chunks (contexts 0 and 1024).
+
+Prints one JSON line. ``roofline`` describes the dominant kernel: average duration from
+hipEvents recorded by the library on the kernel's own stream during the timed steps, and
+algorithmic bytes (each visible K/V position read once, Q read once, O written once) or
+algorithmic flops (unmasked pairs only). ``traffic`` comes from the committed rocprofv3
+counter summary of that kernel (profiles/*_pmc.json) and is null when the kernel source has
+changed since the counters were taken. ``cpu_baseline`` times the fp64 oracle on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+
+
+def algorithmic(wl, step):
+    """Bytes and flops the method must move/compute for this step (per launch)."""
+    import numpy as np
+    e = 2 if wl.dtype == "bf16" else 4
+    q = np.diff(step.cu_q_lens).astype(np.int64)
+    c = step.ctx_lens.astype(np.int64)
+    L = c + q
+    hkv, hq, d = wl.num_kv_heads, wl.num_q_heads, wl.head_dim
+    dec = q == 1
+    out = {}
+    for name, m in (("all", np.ones_like(dec)), ("decode", dec), ("prefill", ~dec)):
+        out[name] = {
+            "bytes": int(e * (2 * (L[m] * hkv * d).sum() + 2 * q[m].sum() * hq * d)),
+            "flops": int(4 * d * hq * (q[m] * c[m] + q[m] * (q[m] + 1) // 2).sum()),
+            "tokens": int(q[m].sum()),
+        }
+    out["append_bytes"] = int(4 * e * q.sum() * hkv * d)
+    return out
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "ragged_continuous_batching_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"decode": ("attn_rows.hip", "cb_device.h", "cb_plan.h"),
+                  "prefill": ("attn_prefill.hip", "cb_device.h", "cb_plan.h")}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None if stale/absent."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(*KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, step, budget_s=25.0):
+    """Times the fp64 oracle on this step's rows (all of them if they fit the budget,
+    else the largest prefix of requests in a fixed order that does)."""
+    import numpy as np
+    import workloads as W
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t_start = time.perf_counter()
+    done_tokens, done_reqs = 0, 0
+    for i in range(step.num_reqs):
+        rid, c = int(step.req_ids[i]), int(step.ctx_lens[i])
+        s, e = int(step.cu_q_lens[i]), int(step.cu_q_lens[i + 1])
+        pos = c + np.arange(e - s)
+        keys = wl.values(W.KIND_K, rid, np.arange(c + e - s))
+        vals = wl.values(W.KIND_V, rid, np.arange(c + e - s))
+        q = wl.values(W.KIND_Q, rid, pos)
+        A.attend(q, keys, vals, pos, wl.scale)
+        done_tokens += e - s
+        done_reqs += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    dt = time.perf_counter() - t_start
+    sample = (f"all {step.num_reqs} requests ({step.num_tokens} rows) of the step" if done_reqs == step.num_reqs
+              else f"first {done_reqs} of {step.num_reqs} requests ({done_tokens} of {step.num_tokens} rows)")
+    return {"value": done_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample + ", fp64 numpy, one call per request incl. gathering inputs", "seconds": round(dt, 3)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU design is described but not built.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from ragged_continuous_batching_amd import cb
+    from ragged_continuous_batching_amd.runner import DeviceRun
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = W.config(args.config)
+    names = {2: "llama2-7b-shaped mixed step (64 decodes + 2x992 prefill chunks)",
+             3: "decode-only GQA (256 decodes, lognormal contexts)",
+             4: "chunked-prefill-heavy (4x2048-token chunks)"}
+    run = DeviceRun(wl, stale=None)
+    base = run.sched
+    # setup: write the cached history once (not timed)
+    probe = base.clone()
+    step0 = probe.build()
+    run.write_history(step0)
+    del probe
+    q, k_new, v_new = run.step_inputs(step0)
+    torch.cuda.synchronize()
+    alg = algorithmic(wl, step0)
+    T = step0.num_tokens
+    o = torch.empty_like(q)
+    ws_bytes = cb.cb_ragged_attention_workspace_size(run.shape, cb.Batch.from_step(step0).struct)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    host_ms = []
+
+    def one_step():
+        t0 = time.perf_counter()
+        s = base.clone()
+        st = s.build()
+        batch = cb.Batch.from_step(st)
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+        cb.cb_kv_append(run.shape, batch.struct, k_new, v_new, run.k_cache, run.v_cache, stream)
+        cb.cb_ragged_attention(run.shape, batch.struct, q, run.k_cache, run.v_cache, wl.scale, o, ws, ws.numel(),
+                               stream)
+        s.commit()
+        return batch, st
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    host_ms.clear()
+    cb.cb_profile_reset()
+    cb.cb_profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    keep = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        keep.append(one_step())
+        if len(keep) > 4:
+            keep.pop(0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cb.cb_profile_enable(False)
+    ms_per_step = wall * 1e3 / args.steps
+    device_ms = ev0.elapsed_time(ev1) / args.steps
+    kernels = {}
+    for name, kid in cb.KERNELS.items():
+        ms, n = cb.cb_profile_read(kid)
+        if n:
+            kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
+    cb.cb_profile_reset()
+
+    dominant = "prefill" if args.config == 4 else "decode"
+    avg_s = kernels[dominant]["avg_us"] * 1e-6
+    if dominant == "decode":
+        achieved = alg["decode"]["bytes"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = alg["prefill"]["flops"] / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = cb.cb_kernel_name(cb.KERNELS[dominant])
+    roof["traffic"] = measured_traffic(dominant, f"config{args.config}")
+
+    result = {
+        "metric": "ragged-attention tokens/s per step",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": names[args.config], "num_tokens": T, "num_reqs": step0.num_reqs,
+                   "num_decode": step0.num_decode, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "token_budget": wl.token_budget,
+                   "seed": wl.seed},
+        "roofline": roof,
+        "device_ms_per_step": round(device_ms, 4),
+        "host_build_ms_per_step": round(float(np.mean(host_ms)), 4),
+        "kernels": kernels,
+        "algorithmic": alg,
+        "attention_tokens_per_s": round(T / (sum(kernels[k]["avg_us"] for k in kernels if k != "append") * 1e-6), 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, step0)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -36,7 +36,8 @@ def common_flags():
 def compile_one(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-x", "hip", "-c", src, "-o", obj, *common_flags(),
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-mcode-object-version=5", "-x", "hip", "-c", src, "-o", obj,
+               *common_flags(),
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
     else:
         rocm = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -58,6 +58,13 @@ class cb_step(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m ragged_continuous_batching_amd.build`")
+    # torch ships its own HIP runtime (same soname, libamdhip64.so.7). Loading torch first
+    # makes libcb.so bind to that copy, so that the process holds one HIP runtime and
+    # device pointers and streams from torch are valid in the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     sig = {
@@ -215,7 +222,7 @@ class Scheduler:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and lib is not None:
             lib.cb_sched_destroy(h)
             self._h = None
 

@@ -41,10 +41,16 @@ struct RowGeom {
 template <int ES>
 __device__ __forceinline__ float dot_chunk(const u32x4& a, const u32x4& b, float acc) {
   if constexpr (ES == 2) {
+    // Words are copied out through memcpy: this compiler miscompiles a bit_cast of a vector
+    // element straight into the dot2 operand (it reuses element 0 for every word).
+    uint32_t aw[4] = {a[0], a[1], a[2], a[3]}, bw[4] = {b[0], b[1], b[2], b[3]};
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[w]), __builtin_bit_cast(bf16x2, b[w]), acc,
-                                            false);
+    for (int w = 0; w < 4; ++w) {
+      bf16x2 x, y;
+      __builtin_memcpy(&x, &aw[w], 4);
+      __builtin_memcpy(&y, &bw[w], 4);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+    }
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w) acc = fmaf(__uint_as_float(a[w]), __uint_as_float(b[w]), acc);
@@ -155,12 +161,12 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
       for (int i = 1; i < NLK; ++i) bm = fmaxf(bm, s[j][i]);
       bm = strided_max<RL>(bm);
       const float m_new = fmaxf(m_run[j], bm);
-      alpha[j] = exp2f(m_run[j] - m_new);
+      alpha[j] = __builtin_amdgcn_exp2f(m_run[j] - m_new);
       m_run[j] = m_new;
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < NLK; ++i) {
-        s[j][i] = exp2f(s[j][i] - m_new);
+        s[j][i] = __builtin_amdgcn_exp2f(s[j][i] - m_new);
         ps += s[j][i];
       }
       l_run[j] = l_run[j] * alpha[j] + ps;
@@ -241,35 +247,64 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
   }
 }
 
-// Merge the splits of one row: one work-group per row, waves stride over query heads.
+// Merge the splits of one row and query head: one wave per (row, head). Lane s holds split
+// s's (max, sum); the weights 2^(m_s - M) are broadcast from their lanes while every lane
+// accumulates D/64 output dims.
 template <int ES, int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const CombineRow row = a.rows[blockIdx.x];
+  const int item = blockIdx.x * 4 + wave_id();
+  if (item >= a.n_rows * a.num_q_heads) return;
   const int lane = lane_id();
-  for (int h = wave_id(); h < a.num_q_heads; h += 4) {
-    float mx = -INFINITY;
-    for (int s = 0; s < row.n_parts; ++s)
-      mx = fmaxf(mx, a.part_ml[(static_cast<int64_t>(row.part_begin + s) * a.num_q_heads + h) * 2]);
-    float den = 0.f;
-    float num[D / 64];
+  const CombineRow row = a.rows[item / a.num_q_heads];
+  const int h = item % a.num_q_heads;
+  const int64_t stride = static_cast<int64_t>(a.num_q_heads);
+  const float* ml = a.part_ml + (static_cast<int64_t>(row.part_begin) * stride + h) * 2;
+  const float* po = a.part_o + (static_cast<int64_t>(row.part_begin) * stride + h) * D + lane;
+
+  float mx = -INFINITY;
+  for (int s = lane; s < row.n_parts; s += 64) mx = fmaxf(mx, ml[s * stride * 2]);
+  mx = strided_max<1>(mx);
+  float den = 0.f;
+  float num[D / 64];
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) num[k] = 0.f;
-    for (int s = 0; s < row.n_parts; ++s) {
-      const int64_t ph = static_cast<int64_t>(row.part_begin + s) * a.num_q_heads + h;
-      const float w = exp2f(a.part_ml[ph * 2] - mx);
-      den = fmaf(w, a.part_ml[ph * 2 + 1], den);
-#pragma unroll
-      for (int k = 0; k < D / 64; ++k) num[k] = fmaf(w, a.part_o[ph * D + k * 64 + lane], num[k]);
+  for (int k = 0; k < D / 64; ++k) num[k] = 0.f;
+  for (int s0 = 0; s0 < row.n_parts; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < row.n_parts) {
+      w = __builtin_amdgcn_exp2f(ml[s * stride * 2] - mx);
+      den = fmaf(w, ml[s * stride * 2 + 1], den);
     }
-    const float inv = 1.f / den;
-    const int64_t base = (static_cast<int64_t>(row.token) * a.num_q_heads + h) * D;
+    const int n = min(64, row.n_parts - s0);
+    int t = 0;
+    for (; t + 4 <= n; t += 4) {
+      float wt[4], v[4][D / 64];
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      if constexpr (ES == 2)
-        static_cast<uint16_t*>(a.o)[base + k * 64 + lane] = to_bf16_bits(num[k] * inv);
-      else
-        static_cast<float*>(a.o)[base + k * 64 + lane] = num[k] * inv;
+      for (int u = 0; u < 4; ++u) {
+        wt[u] = __shfl(w, t + u);
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) v[u][k] = po[(s0 + t + u) * stride * D + k * 64];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) num[k] = fmaf(wt[u], v[u][k], num[k]);
     }
+    for (; t < n; ++t) {
+      const float wt = __shfl(w, t);
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) num[k] = fmaf(wt, po[(s0 + t) * stride * D + k * 64], num[k]);
+    }
+  }
+  den = strided_sum<1>(den);
+  const float inv = 1.f / den;
+  const int64_t base = (static_cast<int64_t>(row.token) * a.num_q_heads + h) * D + lane;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) {
+    if constexpr (ES == 2)
+      static_cast<uint16_t*>(a.o)[base + k * 64] = to_bf16_bits(num[k] * inv);
+    else
+      static_cast<float*>(a.o)[base + k * 64] = num[k] * inv;
   }
 }
 
@@ -302,7 +337,8 @@ hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hi
   if (a.n_rows == 0) return hipSuccess;
   auto k = elem_bytes == 2 ? (head_dim == 128 ? combine_kernel<2, 128> : combine_kernel<2, 64>)
                            : (head_dim == 128 ? combine_kernel<4, 128> : combine_kernel<4, 64>);
-  hipLaunchKernelGGL(k, dim3(a.n_rows), dim3(256), 0, s, a);
+  const int64_t waves = static_cast<int64_t>(a.n_rows) * a.num_q_heads;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
