@@ -115,6 +115,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
+                         "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -130,6 +133,13 @@ def main(argv=None):
     from ragged_continuous_batching_amd.runner import DeviceRun
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     wl = W.config(args.config)
     names = {2: "llama2-7b-shaped mixed step (64 decodes + 2x992 prefill chunks)",
              3: "decode-only GQA (256 decodes, lognormal contexts)",
