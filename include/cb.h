@@ -105,7 +105,8 @@ int cb_kv_append(const cb_shape* shape, const cb_batch* batch, const void* k_new
  * Ragged attention (the operation at the top of this file).
  *   q        device [num_tokens, Hq, head_dim]
  *   k_cache, v_cache  device caches, already holding this step's keys/values
- *   scale    multiplies Q.K before the softmax (the pages show none; 1/sqrt(D) is usual)
+ *   scale    multiplies Q.K before the softmax (the pages show none; 1/sqrt(D) is usual);
+ *            must be positive and finite
  *   o        device [num_tokens, Hq, head_dim], written in full (dtype of the shape)
  *   workspace  device scratch of at least cb_ragged_attention_workspace_size() bytes,
  *            256-byte aligned, owned by the caller. It must not be shared by two calls in
@@ -128,8 +129,13 @@ const char* cb_last_error(void);
 const char* cb_version(void);
 
 /* Tuning knobs (process-wide, host-side). Keys:
- *   "split_blocks"   KV blocks per split of a decode row; 0 = automatic (default)
+ *   "split_blocks"   KV blocks per split of a decode row, at most 64; 0 = automatic (default)
  *   "target_waves"   automatic split sizing aims for at least this many wave items
+ *   "overlap_prefill" 1 = run prefill tiles on an internal side stream (forked from and
+ *                    joined back to `stream`) concurrently with decode rows; 0 (default)
+ *                    runs them one after the other on `stream`
+ *   "xcds"           number of XCDs work-groups are dispatched over round-robin (8 on
+ *                    MI355X); prefill tiles that share keys are placed on one XCD
  * Returns CB_ERR_INVALID_ARG for an unknown key or a negative value. */
 int cb_set_tuning(const char* key, int32_t value);
 

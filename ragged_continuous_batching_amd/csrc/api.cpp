@@ -33,6 +33,8 @@ constexpr double kLog2e = 1.4426950408889634;
 struct Tuning {
   int32_t split_blocks = 0;       // 0 = automatic
   int32_t target_waves = 16384;
+  int32_t overlap_prefill = 0;    // 1 = run prefill tiles on a side stream beside decode rows
+  int32_t xcds = 8;               // XCDs that work-groups are dispatched over (MI355X: 8)
 };
 Tuning g_tuning;
 
@@ -108,6 +110,31 @@ int upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
   return CB_OK;
 }
 
+// ---- side stream for running prefill tiles beside the decode rows ----------------------
+// One non-blocking stream (default priority) and a fork/join event pair per device.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::vector<SideStream> g_side;
+
+int side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CB_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if (static_cast<int>(g_side.size()) <= dev) g_side.resize(dev + 1);
+  SideStream& ss = g_side[dev];
+  if (!ss.stream) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return fail(CB_ERR_HIP, "could not create the side stream");
+  }
+  *out = &ss;
+  return CB_OK;
+}
+
 // ---- validation -------------------------------------------------------------------------
 inline int elem_bytes(const cb_shape* s) { return s->dtype == CB_BF16 ? 2 : 4; }
 inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
@@ -178,6 +205,8 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
 
   // rows that take the split-K path, longest first
   struct Row { int32_t token, req, kv_len; };
+  struct PrefillGroup { std::vector<PrefillItem> items; int64_t cost = 0; };
+  std::vector<PrefillGroup> groups;
   std::vector<Row> rows;
   int64_t total_blocks = 0;
   for (int32_t r = 0; r < b->num_reqs; ++r) {
@@ -189,25 +218,52 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
         total_blocks += ceil_div(c + i + 1, kBlockSize);
       }
     } else {
+      // one group per (request, kv head): all its q-tiles and query heads read the same
+      // key/value tiles, so they are kept on one XCD (shared L2) and run side by side
       const int32_t n_qt = ceil_div(q, kPrefillRows);
-      for (int32_t qt = 0; qt < n_qt; ++qt) {
-        const int32_t qb = qt * kPrefillRows;
-        const int32_t keys = c + std::min(qb + kPrefillRows, q);
-        const int32_t tiles = ceil_div(keys, kPrefillKeys);
-        for (int32_t h = 0; h < s->num_q_heads; ++h) p.prefill.push_back({r, qb, h, tiles});
+      for (int32_t g = 0; g < s->num_kv_heads; ++g) {
+        PrefillGroup grp;
+        for (int32_t qt = n_qt - 1; qt >= 0; --qt) {
+          const int32_t qb = qt * kPrefillRows;
+          const int32_t tiles = ceil_div(c + std::min(qb + kPrefillRows, q), kPrefillKeys);
+          for (int32_t hh = 0; hh < q_per_kv; ++hh) {
+            grp.items.push_back({r, qb, g * q_per_kv + hh, tiles});
+            grp.cost += tiles;
+          }
+        }
+        groups.push_back(std::move(grp));
       }
     }
   }
-  std::stable_sort(p.prefill.begin(), p.prefill.end(),
-                   [](const PrefillItem& x, const PrefillItem& y) { return x.kv_tiles > y.kv_tiles; });
+  // Work-groups are dispatched round-robin over the XCDs (block b runs on XCD b % n). Groups
+  // go, longest first, to the XCD with the least work so far; each XCD's queue is then
+  // interleaved into the launch order. Unused slots hold an empty item (req = -1).
+  if (!groups.empty()) {
+    const int nx = std::max(1, g_tuning.xcds);
+    std::stable_sort(groups.begin(), groups.end(),
+                     [](const PrefillGroup& x, const PrefillGroup& y) { return x.cost > y.cost; });
+    std::vector<std::vector<PrefillItem>> queue(nx);
+    std::vector<int64_t> load(nx, 0);
+    for (const PrefillGroup& grp : groups) {
+      const int x = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+      load[x] += grp.cost;
+      queue[x].insert(queue[x].end(), grp.items.begin(), grp.items.end());
+    }
+    size_t depth = 0;
+    for (const auto& qx : queue) depth = std::max(depth, qx.size());
+    p.prefill.assign(depth * nx, PrefillItem{-1, 0, 0, 0});
+    for (int x = 0; x < nx; ++x)
+      for (size_t k = 0; k < queue[x].size(); ++k) p.prefill[k * nx + x] = queue[x][k];
+  }
   std::stable_sort(rows.begin(), rows.end(), [](const Row& x, const Row& y) { return x.kv_len > y.kv_len; });
 
   int32_t split = g_tuning.split_blocks;
   if (split <= 0) {
     const int64_t units = total_blocks * s->num_kv_heads * p.n_sub;
     const int64_t target = std::max<int32_t>(g_tuning.target_waves, 1);
-    split = static_cast<int32_t>(std::clamp<int64_t>((units + target - 1) / target, 4, 64));
+    split = static_cast<int32_t>(std::clamp<int64_t>((units + target - 1) / target, 4, kMaxSplitBlocks));
   }
+  split = std::min(split, kMaxSplitBlocks);
   for (const Row& row : rows) {
     const int32_t nb = ceil_div(row.kv_len, kBlockSize);
     const int32_t ns = ceil_div(nb, split);
@@ -245,6 +301,10 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.split_blocks = value;
   } else if (std::strcmp(key, "target_waves") == 0) {
     g_tuning.target_waves = value;
+  } else if (std::strcmp(key, "overlap_prefill") == 0) {
+    g_tuning.overlap_prefill = value != 0;
+  } else if (std::strcmp(key, "xcds") == 0) {
+    g_tuning.xcds = std::max<int32_t>(1, value);
   } else {
     return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: unknown key '%s'", key);
   }
@@ -334,6 +394,8 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
   if ((st = check_batch(shape, batch))) return st;
   if (batch->num_tokens == 0) return CB_OK;
   if (!q || !k_cache || !v_cache || !o) return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: NULL tensor");
+  if (!(scale > 0.f) || !(scale < 3.0e38f))
+    return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: scale must be positive and finite");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: tensors must be 16-byte aligned");
   Plan p;
@@ -356,12 +418,26 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
   const int eb = elem_bytes(shape);
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
   hipError_t e = hipSuccess;
+  // Prefill tiles (MFMA-bound) and decode rows (HBM-bound) touch disjoint rows of O. With
+  // "overlap_prefill" set, the prefill kernel runs on a side stream forked from `stream` and
+  // joined back before the call returns, so the two can share the device. It is off by
+  // default: measured on config 2, co-resident prefill work-groups slowed the decode kernel
+  // more than the overlap saved.
+  hipStream_t ps = s;
+  SideStream* side = nullptr;
+  const bool fork = g_tuning.overlap_prefill && !p.prefill.empty() && !p.splits.empty();
+  if (fork) {
+    if ((st = side_stream(&side))) return st;
+    ps = side->stream;
+    if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(ps, side->fork, 0) != hipSuccess)
+      return fail(CB_ERR_HIP, "cb_ragged_attention: fork failed");
+  }
   if (!p.prefill.empty()) {
     PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
                    batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
                    shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2};
-    ProfScope ps(CB_KERNEL_PREFILL, s);
-    e = launch_prefill(pa, shape->head_dim, s);
+    ProfScope prof(CB_KERNEL_PREFILL, ps);
+    e = launch_prefill(pa, shape->head_dim, ps);
   }
   if (e == hipSuccess && !p.splits.empty()) {
     RowArgs ra{q, k_cache, v_cache, o,
@@ -369,7 +445,7 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
                reinterpret_cast<const RowSplit*>(ws), batch->block_tables,
                static_cast<int32_t>(p.splits.size()) * shape->num_kv_heads * p.n_sub,
                shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2};
-    ProfScope ps(CB_KERNEL_DECODE, s);
+    ProfScope prof(CB_KERNEL_DECODE, s);
     e = launch_rows(ra, eb, shape->head_dim, p.group, s);
   }
   if (e == hipSuccess && !p.combine.empty()) {
@@ -377,8 +453,12 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
                    reinterpret_cast<const float*>(ws + p.off_part_ml),
                    reinterpret_cast<const CombineRow*>(ws + p.off_combine), static_cast<int32_t>(p.combine.size()),
                    shape->num_q_heads};
-    ProfScope ps(CB_KERNEL_COMBINE, s);
+    ProfScope prof(CB_KERNEL_COMBINE, s);
     e = launch_combine(ca, eb, shape->head_dim, s);
+  }
+  if (fork) {
+    if (hipEventRecord(side->join, ps) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+      return fail(CB_ERR_HIP, "cb_ragged_attention: join failed");
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_ragged_attention: launch failed: %s", hipGetErrorString(e));
   return CB_OK;

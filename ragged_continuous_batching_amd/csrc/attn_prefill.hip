@@ -42,12 +42,14 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using Geo = PrefillGeom<D>;
   constexpr int KS = Geo::KS, VS = Geo::VS, KCH = Geo::KCH, VCH = Geo::VCH, DCH = Geo::DCH, DT = Geo::DT;
   __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
+  __shared__ int32_t lds_bt[kPrefillLdsBlocks];   // block ids of the keys this WG reads
 
   const PrefillItem it = a.items[blockIdx.x];
+  if (it.req < 0) return;                                     // padding slot of the launch order
   const int r = it.req, h = it.head;
   const int hkv = a.num_kv_heads;
   const int g = h / (a.num_q_heads / hkv);
@@ -65,6 +67,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int wg_keys = c + min(it.q_begin + kPrefillRows - 1, nq - 1) + 1;
   const int n_tiles = (wg_keys + kPrefillKeys - 1) / kPrefillKeys;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
+  // Stage the block ids once, so that each tile's loads depend on an LDS read rather than
+  // on a global load (keys past kPrefillLdsBlocks*16 fall back to the global table).
+  const int n_bt = min((wg_keys + kBlockSize - 1) / kBlockSize, kPrefillLdsBlocks);
+  for (int i = threadIdx.x; i < n_bt; i += 256) {
+    const int blk = bt[i];
+    lds_bt[i] = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
+  }
+  __syncthreads();
+  auto block_of = [&](int pos) -> int {
+    const int i = pos / kBlockSize;
+    if (i < kPrefillLdsBlocks) return lds_bt[i];
+    const int blk = bt[i];
+    return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
+  };
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
@@ -91,8 +107,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int pos = j * kPrefillKeys + key;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (pos < kv_len) {
-        int blk = bt[pos / kBlockSize];
-        if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = 0;
+        const int blk = block_of(pos);
         v = *reinterpret_cast<const u32x4*>(kc + (static_cast<int64_t>(blk) * hkv + g) * page_elems +
                                             (pos % kBlockSize) * D + dc * 8);
       }
@@ -105,8 +120,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int pos = j * kPrefillKeys + kq * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (pos < kv_len) {
-        int blk = bt[pos / kBlockSize];
-        if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = 0;
+        const int blk = block_of(pos);
         v = *reinterpret_cast<const u32x4*>(vc + (static_cast<int64_t>(blk) * hkv + g) * page_elems +
                                             d * kBlockSize + (pos % kBlockSize));
         if (pos + 8 > kv_len) {             // the octet straddles the end: clear stale slots
@@ -152,8 +166,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     store_tile(buf);
+    if (j + 1 < n_tiles) load_tile(j + 1);     // in flight across the barrier and the math
     __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
     if (!wave_active || j * kPrefillKeys >= wave_keys) continue;
 
     const uint16_t* kl = lds + buf * Geo::K_TILE;
@@ -161,33 +175,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // S^T for keys [64j, 64j+32) and [64j+32, 64j+64)
     f32x16 st[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
 #pragma unroll
-      for (int dc = 0; dc < DCH; ++dc) {
+    for (int dc = 0; dc < DCH; ++dc)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {   // two independent accumulation chains, interleaved
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + col) * KS + dc * 16 + grp * 8);
         st[kt] = mfma32(ka, qf[dc], st[kt]);
       }
+    // causal mask on diagonal tiles, then the online softmax on raw scores: the scale is
+    // positive, so max(scale*s) = scale*max(s) and it folds into one fma before exp2.
+    const bool diag = __builtin_amdgcn_readfirstlane(j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0);
+    if (diag) {
+      const int rel = qpos - j * kPrefillKeys - grp * 4;    // key offset limit for this lane
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt * 32 + (i >> 2) * 8 + (i & 3) > rel) st[kt][i] = -INFINITY;
     }
-    // scale, causal mask on diagonal tiles, online softmax (this lane's query = column)
-    const bool diag = j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0;
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = st[kt][i] * a.scale_log2;
-        if (diag) {
-          const int kpos = j * kPrefillKeys + kt * 32 + (i >> 2) * 8 + grp * 4 + (i & 3);
-          s = kpos <= qpos ? s : -INFINITY;
-        }
-        st[kt][i] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over lanes l and l^32
+    }
+    const float m_new = fmaxf(m_run, mx * a.scale_log2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const bool rescale = __builtin_amdgcn_readfirstlane(__ballot(m_new != m_run) != 0);
     m_run = m_new;
     float psum = 0.f;
     bf16x8 pb[4];
@@ -198,18 +218,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(st[kt][half * 8 + 2 * e] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(st[kt][half * 8 + 2 * e + 1] - m_new);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][half * 8 + 2 * e], a.scale_log2, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][half * 8 + 2 * e + 1], a.scale_log2, -m_new));
           psum += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
         pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       }
     l_run = l_run * alpha + psum;
+    if (rescale) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -225,7 +247,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 
   if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   if (qrow >= nq) return;
   const float inv = 1.f / l_tot;
   uint16_t* op = static_cast<uint16_t*>(a.o) + (static_cast<int64_t>(t0 + qrow) * a.num_q_heads + h) * D;
