@@ -136,6 +136,8 @@ const char* cb_version(void);
  *                    runs them one after the other on `stream`
  *   "xcds"           number of XCDs work-groups are dispatched over round-robin (8 on
  *                    MI355X); prefill tiles that share keys are placed on one XCD
+ *   "prefill_touch"  1 = the prefill kernel also loads one dword per cache line of the key
+ *                    tile two steps ahead (warms L2); 0 (default) = off
  * Returns CB_ERR_INVALID_ARG for an unknown key or a negative value. */
 int cb_set_tuning(const char* key, int32_t value);
 

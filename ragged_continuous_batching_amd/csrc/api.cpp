@@ -35,6 +35,7 @@ struct Tuning {
   int32_t target_waves = 16384;
   int32_t overlap_prefill = 0;    // 1 = run prefill tiles on a side stream beside decode rows
   int32_t xcds = 8;               // XCDs that work-groups are dispatched over (MI355X: 8)
+  int32_t prefill_touch = 0;      // 1: prefill pulls key tiles two steps ahead toward L2
 };
 Tuning g_tuning;
 
@@ -305,6 +306,8 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.overlap_prefill = value != 0;
   } else if (std::strcmp(key, "xcds") == 0) {
     g_tuning.xcds = std::max<int32_t>(1, value);
+  } else if (std::strcmp(key, "prefill_touch") == 0) {
+    g_tuning.prefill_touch = value != 0;
   } else {
     return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: unknown key '%s'", key);
   }
@@ -435,7 +438,8 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
   if (!p.prefill.empty()) {
     PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
                    batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
-                   shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2};
+                   shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2,
+                   g_tuning.prefill_touch};
     ProfScope prof(CB_KERNEL_PREFILL, ps);
     e = launch_prefill(pa, shape->head_dim, ps);
   }

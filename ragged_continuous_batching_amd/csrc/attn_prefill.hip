@@ -31,8 +31,6 @@ struct PrefillGeom {
   static constexpr int K_TILE = kPrefillKeys * KS;
   static constexpr int V_TILE = D * VS;
   static constexpr int LDS_ELEMS = 2 * (K_TILE + V_TILE);
-  static constexpr int KCH = kPrefillKeys * D / 8 / 256;   // 16-byte K chunks per thread
-  static constexpr int VCH = D * kPrefillKeys / 8 / 256;   // 16-byte V chunks per thread
   static constexpr int DCH = D / 16;                  // MFMA k-steps over the head dim
   static constexpr int DT = D / 32;                   // 32-wide output tiles over the head dim
 };
@@ -44,7 +42,7 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using Geo = PrefillGeom<D>;
-  constexpr int KS = Geo::KS, VS = Geo::VS, KCH = Geo::KCH, VCH = Geo::VCH, DCH = Geo::DCH, DT = Geo::DT;
+  constexpr int KS = Geo::KS, VS = Geo::VS, DCH = Geo::DCH, DT = Geo::DT;
   __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
   __shared__ int32_t lds_bt[kPrefillLdsBlocks];   // block ids of the keys this WG reads
 
@@ -68,19 +66,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int n_tiles = (wg_keys + kPrefillKeys - 1) / kPrefillKeys;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
   // Stage the block ids once, so that each tile's loads depend on an LDS read rather than
-  // on a global load (keys past kPrefillLdsBlocks*16 fall back to the global table).
+  // on a global load. Keys past kPrefillLdsBlocks*16 read the global table instead (a
+  // uniform per-tile branch).
   const int n_bt = min((wg_keys + kBlockSize - 1) / kBlockSize, kPrefillLdsBlocks);
   for (int i = threadIdx.x; i < n_bt; i += 256) {
     const int blk = bt[i];
     lds_bt[i] = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
   }
   __syncthreads();
-  auto block_of = [&](int pos) -> int {
-    const int i = pos / kBlockSize;
-    if (i < kPrefillLdsBlocks) return lds_bt[i];
-    const int blk = bt[i];
-    return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-  };
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
@@ -97,58 +90,59 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // global -> registers for key tile j (zeros for positions >= kv_len)
-  u32x4 kreg[KCH], vreg[VCH];
+  // global -> registers for key tile j. Every load instruction of a wave reads one page of
+  // the tile (positions 64j+16p .. +15), so its block id is a scalar and each thread's offset
+  // inside the page is fixed: K row tl/(D/8), chunk tl%(D/8); V^T bytes tl*16 (d-row tl/2,
+  // key octet tl%2). At D = 128 a page is one 16-byte chunk per thread (4 loads cover the 4
+  // pages); at D = 64 the two halves of the work-group take two pages per load. Only the
+  // tile that reaches wg_keys (the last key any row of this work-group sees) clamps pages
+  // and zeroes positions past it.
+  constexpr int PPL = 128 / D;                                     // pages per load
+  constexpr int NL = 4 / PPL;                                      // loads per tile
+  u32x4 kreg[NL], vreg[NL];
+  const int tl = tid % (256 / PPL);                                // thread within its page
+  auto page_block = [&](int pidx) -> int {                         // block id of key page pidx
+    const int i = min(pidx, (wg_keys - 1) / kBlockSize);
+    int blk;
+    if (i < kPrefillLdsBlocks) {
+      blk = lds_bt[i];
+    } else {
+      blk = bt[i];
+      blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
+    }
+    return __builtin_amdgcn_readfirstlane(blk);
+  };
   auto load_tile = [&](int j) {
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int cid = tid + 256 * u;
-      const int key = cid / (D / 8), dc = cid % (D / 8);
-      const int pos = j * kPrefillKeys + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (pos < kv_len) {
-        const int blk = block_of(pos);
-        v = *reinterpret_cast<const u32x4*>(kc + (static_cast<int64_t>(blk) * hkv + g) * page_elems +
-                                            (pos % kBlockSize) * D + dc * 8);
-      }
-      kreg[u] = v;
+    for (int u = 0; u < NL; ++u) {
+      const int page = u * PPL + tid / (256 / PPL);                // wave-uniform
+      const int64_t base = (static_cast<int64_t>(page_block(j * 4 + page)) * hkv + g) * page_elems;
+      kreg[u] = *reinterpret_cast<const u32x4*>(kc + base + (tl / (D / 8)) * D + (tl % (D / 8)) * 8);
+      vreg[u] = *reinterpret_cast<const u32x4*>(vc + base + tl * 8);
     }
+    if ((j + 1) * kPrefillKeys > wg_keys) {        // the last tile: zero keys >= wg_keys
 #pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int cid = tid + 256 * u;
-      const int d = cid / 8, kq = cid % 8;                      // key octet kq of the tile
-      const int pos = j * kPrefillKeys + kq * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (pos < kv_len) {
-        const int blk = block_of(pos);
-        v = *reinterpret_cast<const u32x4*>(vc + (static_cast<int64_t>(blk) * hkv + g) * page_elems +
-                                            d * kBlockSize + (pos % kBlockSize));
-        if (pos + 8 > kv_len) {             // the octet straddles the end: clear stale slots
+      for (int u = 0; u < NL; ++u) {
+        const int page = u * PPL + tid / (256 / PPL);
+        const int kpos = j * kPrefillKeys + page * kBlockSize + tl / (D / 8);
+        if (kpos >= wg_keys) kreg[u] = u32x4{0u, 0u, 0u, 0u};
+        const int vpos = j * kPrefillKeys + page * kBlockSize + (tl % 2) * 8;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int p0 = pos + 2 * w;
-            uint32_t keep = (p0 < kv_len ? 0x0000ffffu : 0u) | (p0 + 1 < kv_len ? 0xffff0000u : 0u);
-            v[w] &= keep;
-          }
+        for (int w = 0; w < 4; ++w) {
+          const int p0 = vpos + 2 * w;
+          vreg[u][w] &= (p0 < wg_keys ? 0x0000ffffu : 0u) | (p0 + 1 < wg_keys ? 0xffff0000u : 0u);
         }
       }
-      vreg[u] = v;
     }
   };
   auto store_tile = [&](int buf) {
     uint16_t* kl = lds + buf * Geo::K_TILE;
     uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int cid = tid + 256 * u;
-      const int key = cid / (D / 8), dc = cid % (D / 8);
-      *reinterpret_cast<u32x4*>(kl + key * KS + dc * 8) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int cid = tid + 256 * u;
-      const int d = cid / 8, kq = cid % 8;
-      u32x2* dst = reinterpret_cast<u32x2*>(vl + d * VS + kq * 8);
+    for (int u = 0; u < NL; ++u) {
+      const int page = u * PPL + tid / (256 / PPL);
+      *reinterpret_cast<u32x4*>(kl + (page * kBlockSize + tl / (D / 8)) * KS + (tl % (D / 8)) * 8) = kreg[u];
+      u32x2* dst = reinterpret_cast<u32x2*>(vl + (tl / 2) * VS + page * kBlockSize + (tl % 2) * 8);
       dst[0] = u32x2{vreg[u][0], vreg[u][1]};
       dst[1] = u32x2{vreg[u][2], vreg[u][3]};
     }
@@ -205,10 +199,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over lanes l and l^32
     }
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const bool rescale = __builtin_amdgcn_readfirstlane(__ballot(m_new != m_run) != 0);
-    m_run = m_new;
+    // Lazy rescaling: the reference max only moves when some lane's max grew by more than
+    // 8 (log2 units). Until then probabilities may reach 2^8, which fp32 sums and bf16 P
+    // hold exactly as well as values below 1; O and l share the same reference, so the
+    // final O / l is unchanged.
+    const float m_cand = fmaxf(m_run, mx * a.scale_log2);
+    if (__builtin_amdgcn_readfirstlane(__ballot(m_cand > m_run + 8.f) != 0)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
+      m_run = m_cand;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float m_new = m_run;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -225,13 +230,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
         pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       }
-    l_run = l_run * alpha + psum;
-    if (rescale) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-    }
+    l_run += psum;
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
