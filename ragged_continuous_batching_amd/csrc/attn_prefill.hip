@@ -27,13 +27,18 @@ namespace cb {
 template <int D>
 struct PrefillGeom {
   static constexpr int KS = D + 8;                    // K tile row stride (elements)
-  static constexpr int VS = kPrefillKeys + 4;         // V^T tile row stride (elements)
+  static constexpr int VS = kPrefillKeys + 8;         // V^T tile row stride (elements, 16-B rows)
   static constexpr int K_TILE = kPrefillKeys * KS;
   static constexpr int V_TILE = D * VS;
   static constexpr int LDS_ELEMS = 2 * (K_TILE + V_TILE);
   static constexpr int DCH = D / 16;                  // MFMA k-steps over the head dim
   static constexpr int DT = D / 32;                   // 32-wide output tiles over the head dim
 };
+
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x0002;
+constexpr int kSchedMfma = 0x0008;
+constexpr int kSchedDsRead = 0x0100;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -142,9 +147,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int u = 0; u < NL; ++u) {
       const int page = u * PPL + tid / (256 / PPL);
       *reinterpret_cast<u32x4*>(kl + (page * kBlockSize + tl / (D / 8)) * KS + (tl % (D / 8)) * 8) = kreg[u];
-      u32x2* dst = reinterpret_cast<u32x2*>(vl + (tl / 2) * VS + page * kBlockSize + (tl % 2) * 8);
-      dst[0] = u32x2{vreg[u][0], vreg[u][1]};
-      dst[1] = u32x2{vreg[u][2], vreg[u][3]};
+      // Inside each 16-key page, key k sits at position (k&3) + 4*(k>>3) + 8*((k>>2)&1):
+      // positions 0..7 then hold keys 0-3 and 8-11, positions 8..15 keys 4-7 and 12-15, the
+      // two key sets that lanes 0-31 and 32-63 take in one 32x32x16 step (the S^T accumulator
+      // layout). The thread's octet tl%2 = h (keys 8h..8h+7) goes to positions 4h.. and 8+4h..
+      uint16_t* vrow = vl + (tl / 2) * VS + page * kBlockSize + (tl % 2) * 4;
+      *reinterpret_cast<u32x2*>(vrow) = u32x2{vreg[u][0], vreg[u][1]};
+      *reinterpret_cast<u32x2*>(vrow + 8) = u32x2{vreg[u][2], vreg[u][3]};
     }
   };
 
@@ -156,18 +165,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const int qpos = c + qrow;
 
-  load_tile(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    store_tile(buf);
-    if (j + 1 < n_tiles) load_tile(j + 1);     // in flight across the barrier and the math
-    __syncthreads();
-    if (!wave_active || j * kPrefillKeys >= wave_keys) continue;
-
+  // S^T for the 64 keys of the tile in LDS buffer `buf`: two 32-key accumulators
+  auto compute_s = [&](int buf, f32x16 (&st)[2]) {
     const uint16_t* kl = lds + buf * Geo::K_TILE;
-    const uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
-    // S^T for keys [64j, 64j+32) and [64j+32, 64j+64)
-    f32x16 st[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -179,30 +179,36 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + col) * KS + dc * 16 + grp * 8);
         st[kt] = mfma32(ka, qf[dc], st[kt]);
       }
-    // causal mask on diagonal tiles, then the online softmax on raw scores: the scale is
-    // positive, so max(scale*s) = scale*max(s) and it folds into one fma before exp2.
+  };
+
+  // One key tile j whose scores are in s_cur: mask, softmax, O += V P. The scores of tile
+  // j+1 (other LDS buffer) are computed into s_next in the same straight-line block as the
+  // exp2 work of tile j, so the matrix core and the vector ALU overlap within the wave.
+  auto tile_step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    const int buf = j & 1;
+    if (!wave_active || j * kPrefillKeys >= wave_keys) return;
     const bool diag = __builtin_amdgcn_readfirstlane(j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0);
-    if (diag) {
-      const int rel = qpos - j * kPrefillKeys - grp * 4;    // key offset limit for this lane
+    if (diag) {                                  // causal mask, only on tiles crossing it
+      const int rel = qpos - j * kPrefillKeys - grp * 4;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kt * 32 + (i >> 2) * 8 + (i & 3) > rel) st[kt][i] = -INFINITY;
+          if (kt * 32 + (i >> 2) * 8 + (i & 3) > rel) s_cur[kt][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kt][i]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over lanes l and l^32
     }
     // Lazy rescaling: the reference max only moves when some lane's max grew by more than
     // 8 (log2 units). Until then probabilities may reach 2^8, which fp32 sums and bf16 P
-    // hold exactly as well as values below 1; O and l share the same reference, so the
-    // final O / l is unchanged.
+    // hold as well as values below 1; O and l share the reference, so O / l is unchanged.
+    // The scale is positive, so max(scale*s) = scale*max(s) and it folds into the fma.
     const float m_cand = fmaxf(m_run, mx * a.scale_log2);
     if (__builtin_amdgcn_readfirstlane(__ballot(m_cand > m_run + 8.f) != 0)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
@@ -213,7 +219,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
     }
-    const float m_new = m_run;
+    compute_s(buf ^ 1, s_next);
+    const float m_ref = m_run;
     float psum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
@@ -223,25 +230,71 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kt][half * 8 + 2 * e], a.scale_log2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kt][half * 8 + 2 * e + 1], a.scale_log2, -m_new));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][half * 8 + 2 * e], a.scale_log2, -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][half * 8 + 2 * e + 1], a.scale_log2, -m_ref));
           psum += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
         pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       }
     l_run += psum;
-    // O^T += V^T P^T over four 16-key steps
+    // O^T += V^T P^T over four 16-key steps; one 16-byte read per A operand (the key order
+    // inside each 16-key page of the V^T tile matches the P layout, see store_tile)
+    const uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vrow = vl + (dt * 32 + col) * VS + grp * 4;
+      const uint16_t* vrow = vl + (dt * 32 + col) * VS + grp * 8;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + ks * 16);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + ks * 16 + 8);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + ks * 16);
         oacc[dt] = mfma32(va, pb[ks], oacc[dt]);
       }
+    }
+    // Instruction order for the block above (scheduler groups): the next tile's score
+    // MFMAs alternate with the exp2/pack work of this tile, with each LDS operand read
+    // issued two MFMAs ahead; then the P.V MFMAs, again with reads running ahead.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * DCH; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4 * DT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    }
+  };
+
+  // prologue: tiles 0 and 1 in LDS, the scores of tile 0 computed, tile 2 in flight
+  load_tile(0);
+  store_tile(0);
+  if (n_tiles > 1) load_tile(1);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (wave_active) compute_s(0, sa);
+  if (n_tiles > 1) {
+    store_tile(1);
+    if (n_tiles > 2) load_tile(2);
+  }
+  __syncthreads();
+  // Per tile j: step (reads buffer j&1, scores of j+1 from the other buffer), a barrier
+  // (buffer j&1 is free), tile j+2 from registers into it, the loads of j+3, a barrier.
+  auto advance = [&](int j) {
+    __syncthreads();
+    if (j + 2 < n_tiles) {
+      store_tile(j & 1);
+      if (j + 3 < n_tiles) load_tile(j + 3);
+    }
+    __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile_step(j, sa, sb);
+    advance(j);
+    if (j + 1 < n_tiles) {
+      tile_step(j + 1, sb, sa);
+      advance(j + 1);
     }
   }
 
