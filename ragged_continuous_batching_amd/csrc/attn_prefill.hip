@@ -196,11 +196,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 16; ++i)
           if (kt * 32 + (i >> 2) * 8 + (i & 3) > rel) s_cur[kt][i] = -INFINITY;
     }
-    float mx = -INFINITY;
+    float mq[4];                                 // four independent max chains
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int q = 0; q < 4; ++q) mq[q] = fmaxf(s_cur[q >> 1][(q & 1) * 8], s_cur[q >> 1][(q & 1) * 8 + 1]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kt][i]);
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 2; i < 8; ++i) mq[q] = fmaxf(mq[q], s_cur[q >> 1][(q & 1) * 8 + i]);
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over lanes l and l^32
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
     compute_s(buf ^ 1, s_next);
     const float m_ref = m_run;
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};          // four independent sum chains
     bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -232,24 +235,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][half * 8 + 2 * e], a.scale_log2, -m_ref));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][half * 8 + 2 * e + 1], a.scale_log2, -m_ref));
-          psum += p0 + p1;
+          ps[kt * 2 + half] += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
         pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       }
-    l_run += psum;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // O^T += V^T P^T over four 16-key steps; one 16-byte read per A operand (the key order
     // inside each 16-key page of the V^T tile matches the P layout, see store_tile)
     const uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vrow = vl + (dt * 32 + col) * VS + grp * 8;
+    for (int ks = 0; ks < 4; ++ks)               // DT independent accumulators back to back
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + ks * 16);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (dt * 32 + col) * VS + grp * 8 + ks * 16);
         oacc[dt] = mfma32(va, pb[ks], oacc[dt]);
       }
-    }
     // Instruction order for the block above (scheduler groups): the next tile's score
     // MFMAs alternate with the exp2/pack work of this tile, with each LDS operand read
     // issued two MFMAs ahead; then the P.V MFMAs, again with reads running ahead.
