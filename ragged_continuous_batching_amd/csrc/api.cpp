@@ -36,6 +36,7 @@ struct Tuning {
   int32_t overlap_prefill = 0;    // 1 = run prefill tiles on a side stream beside decode rows
   int32_t xcds = 8;               // XCDs that work-groups are dispatched over (MI355X: 8)
   int32_t prefill_touch = 0;      // 1: prefill pulls key tiles two steps ahead toward L2
+  int32_t decode_group = 8;       // most query heads one decode wave handles (1, 2, 4 or 8)
 };
 Tuning g_tuning;
 
@@ -200,7 +201,10 @@ struct Plan {
 
 void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
   const int q_per_kv = s->num_q_heads / s->num_kv_heads;
-  p.group = q_per_kv >= 8 ? 8 : q_per_kv;
+  // query heads per decode wave: all heads of the group up to decode_group; a larger group
+  // is covered by n_sub waves on adjacent slots, which read the same pages back to back
+  p.group = std::min(q_per_kv, static_cast<int>(g_tuning.decode_group));
+  while (q_per_kv % p.group) p.group /= 2;
   p.n_sub = q_per_kv / p.group;
   const bool mfma_prefill = s->dtype == CB_BF16;
 
@@ -308,6 +312,10 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.xcds = std::max<int32_t>(1, value);
   } else if (std::strcmp(key, "prefill_touch") == 0) {
     g_tuning.prefill_touch = value != 0;
+  } else if (std::strcmp(key, "decode_group") == 0) {
+    if (value != 1 && value != 2 && value != 4 && value != 8)
+      return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: decode_group must be 1, 2, 4 or 8");
+    g_tuning.decode_group = value;
   } else {
     return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: unknown key '%s'", key);
   }
