@@ -138,6 +138,8 @@ const char* cb_version(void);
  *                    MI355X); prefill tiles that share keys are placed on one XCD
  *   "prefill_touch"  1 = the prefill kernel also loads one dword per cache line of the key
  *                    tile two steps ahead (warms L2); 0 (default) = off
+ *   "decode_mfma"    1 (default) = decode rows of bf16 models with 4 or more query heads per
+ *                    kv head use the matrix-core kernel; 0 = the vector-ALU kernel
  *   "decode_group"   most query heads of one kv head that a decode wave handles (1, 2, 4
  *                    or 8; default 8). Smaller groups use fewer registers per wave; the
  *                    waves of one kv head then read the same pages back to back.

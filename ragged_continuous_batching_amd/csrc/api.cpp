@@ -24,6 +24,7 @@ hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int head_dim, h
 hipError_t launch_rows(const RowArgs& a, int elem_bytes, int head_dim, int group, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_rows_mfma(const RowArgs& a, int head_dim, hipStream_t s);
 
 namespace {
 
@@ -37,6 +38,7 @@ struct Tuning {
   int32_t xcds = 8;               // XCDs that work-groups are dispatched over (MI355X: 8)
   int32_t prefill_touch = 0;      // 1: prefill pulls key tiles two steps ahead toward L2
   int32_t decode_group = 8;       // most query heads one decode wave handles (1, 2, 4 or 8)
+  int32_t decode_mfma = 1;        // 1: grouped-query decode (4+ heads per kv head) on MFMA
 };
 Tuning g_tuning;
 
@@ -195,6 +197,7 @@ struct Plan {
   std::vector<PrefillItem> prefill;
   int32_t n_parts = 0;
   int group = 1;         // query heads per decode wave
+  bool mfma_decode = false;  // decode rows on the MFMA kernel
   int n_sub = 1;         // decode waves per kv head
   size_t off_combine = 0, off_prefill = 0, plan_bytes = 0, off_part_o = 0, off_part_ml = 0, total = 0;
 };
@@ -203,8 +206,13 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
   const int q_per_kv = s->num_q_heads / s->num_kv_heads;
   // query heads per decode wave: all heads of the group up to decode_group; a larger group
   // is covered by n_sub waves on adjacent slots, which read the same pages back to back
-  p.group = std::min(q_per_kv, static_cast<int>(g_tuning.decode_group));
-  while (q_per_kv % p.group) p.group /= 2;
+  p.mfma_decode = s->dtype == CB_BF16 && q_per_kv >= 4 && g_tuning.decode_mfma;
+  if (p.mfma_decode) {          // up to 16 heads fill the columns of one 16x16 tile
+    p.group = q_per_kv % 16 == 0 ? 16 : (q_per_kv % 8 == 0 ? 8 : 4);
+  } else {
+    p.group = std::min(q_per_kv, static_cast<int>(g_tuning.decode_group));
+    while (q_per_kv % p.group) p.group /= 2;
+  }
   p.n_sub = q_per_kv / p.group;
   const bool mfma_prefill = s->dtype == CB_BF16;
 
@@ -312,6 +320,8 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.xcds = std::max<int32_t>(1, value);
   } else if (std::strcmp(key, "prefill_touch") == 0) {
     g_tuning.prefill_touch = value != 0;
+  } else if (std::strcmp(key, "decode_mfma") == 0) {
+    g_tuning.decode_mfma = value != 0;
   } else if (std::strcmp(key, "decode_group") == 0) {
     if (value != 1 && value != 2 && value != 4 && value != 8)
       return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: decode_group must be 1, 2, 4 or 8");
@@ -456,9 +466,10 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
                reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml),
                reinterpret_cast<const RowSplit*>(ws), batch->block_tables,
                static_cast<int32_t>(p.splits.size()) * shape->num_kv_heads * p.n_sub,
-               shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2};
+               shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2,
+               p.group};
     ProfScope prof(CB_KERNEL_DECODE, s);
-    e = launch_rows(ra, eb, shape->head_dim, p.group, s);
+    e = p.mfma_decode ? launch_rows_mfma(ra, shape->head_dim, s) : launch_rows(ra, eb, shape->head_dim, p.group, s);
   }
   if (e == hipSuccess && !p.combine.empty()) {
     CombineArgs ca{o, reinterpret_cast<const float*>(ws + p.off_part_o),

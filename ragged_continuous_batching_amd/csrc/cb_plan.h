@@ -62,9 +62,10 @@ struct RowArgs {
   float* part_ml;         // [n_parts, Hq, 2] fp32: running max (log2 units), sum
   const RowSplit* splits;
   const int32_t* block_tables;
-  int32_t n_items;        // splits * num_kv_heads
+  int32_t n_items;        // splits * num_kv_heads * (query heads per kv head / group)
   int32_t num_q_heads, num_kv_heads, max_blocks, num_blocks;
   float scale_log2;       // scale * log2(e)
+  int32_t group;          // query heads per work item
 };
 
 struct CombineArgs {

@@ -150,6 +150,19 @@ def test_append_is_bit_exact_and_stays_in_its_slots():
     assert torch.isnan(kc.permute(0, 2, 1, 3)[~written]).all()
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (32, 2)])
+def test_gqa_decode_vector_alu_kernel(hq, hkv):
+    """The vector-ALU decode kernel also serves grouped-query rows when the matrix-core
+    kernel is switched off ("decode_mfma" = 0)."""
+    wl = small_workload("long_decode", hq, hkv, 128, "bf16")
+    cb.cb_set_tuning("decode_mfma", 0)
+    try:
+        run, step, batch, o = run_one_step(wl)
+    finally:
+        cb.cb_set_tuning("decode_mfma", 1)
+    check(o, oracle_full(wl, step), "bf16", f"vector-ALU decode Hq={hq} Hkv={hkv}")
+
+
 @pytest.mark.parametrize("split", [4, 7, 64])
 def test_split_count_invariance(split):
     wl = small_workload("long_decode", 8, 2, 128, "bf16")
