@@ -113,7 +113,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="2: mixed step (default), 3: decode-only GQA, 4: chunked prefill, "
+                         "5: the 500-step scheduler trace (steps = trace steps after the warm-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
@@ -133,6 +135,8 @@ def main(argv=None):
     from ragged_continuous_batching_amd.runner import DeviceRun
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.config == 5:
+        return bench_trace(args)
     if args.copy_calibration:
         src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -213,6 +217,8 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
     roof["kernel"] = cb.cb_kernel_name(cb.KERNELS[dominant])
+    if dominant == "decode" and wl.dtype == "bf16" and wl.num_q_heads // wl.num_kv_heads >= 4:
+        roof["kernel"] = "row_attn_mfma_kernel"        # grouped-query decode runs on the matrix cores
     roof["traffic"] = measured_traffic(dominant, f"config{args.config}")
 
     result = {
@@ -241,6 +247,112 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, step0)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_trace(args):
+    """Scheduler-trace replay (Hq=64, Hkv=8, m=4096, Poisson(8) arrivals, 500 steps): every
+    step is built by the step builder, appended and attended. Step inputs come from fixed
+    synthetic Q/K/V buffers of m rows resident in HBM (values do not change the work)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from ragged_continuous_batching_amd import cb
+    from ragged_continuous_batching_amd.runner import DeviceRun
+
+    wl = W.config(5)
+    total_steps = wl.steps
+    warm = min(args.warmup, total_steps - 1)
+    steps = min(args.steps if args.steps != 50 else total_steps - warm, total_steps - warm)
+    run = DeviceRun(wl, stale=None)
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    m = wl.token_budget
+    q = torch.randn(m, wl.num_q_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    k_new = torch.randn(m, wl.num_kv_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    v_new = torch.randn(m, wl.num_kv_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    # dry run of the schedule on a copy: the largest workspace any step needs
+    dry = run.sched.clone()
+    need, alg_dec_bytes, tokens = 0, [], []
+    for kstep in range(total_steps):
+        for r in wl.arrivals[kstep]:
+            dry.add(r.req_id, r.prompt_len, r.out_len)
+        st = dry.build()
+        b = cb.cb_batch(st.num_reqs, st.num_tokens, st.max_blocks_per_req, 256, 256, 256,
+                        st.cu_q_lens.ctypes.data, st.ctx_lens.ctypes.data)
+        need = max(need, cb.cb_ragged_attention_workspace_size(run.shape, b))
+        alg = algorithmic(wl, st)
+        alg_dec_bytes.append(alg["decode"]["bytes"])
+        tokens.append(st.num_tokens)
+        dry.commit()
+    del dry
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sched = run.sched
+
+    def one(kstep):
+        for r in wl.arrivals[kstep]:
+            sched.add(r.req_id, r.prompt_len, r.out_len)
+        st = sched.build()
+        batch = cb.Batch.from_step(st)
+        T = st.num_tokens
+        cb.cb_kv_append(run.shape, batch.struct, k_new, v_new, run.k_cache, run.v_cache, stream)
+        cb.cb_ragged_attention(run.shape, batch.struct, q, run.k_cache, run.v_cache, wl.scale, o, ws, ws.numel(),
+                               stream)
+        sched.commit()
+        return batch, T
+
+    for kstep in range(warm):
+        one(kstep)
+    torch.cuda.synchronize()
+    cb.cb_profile_reset()
+    cb.cb_profile_enable(True)
+    keep = []
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for kstep in range(warm, warm + steps):
+        keep.append(one(kstep))
+        if len(keep) > 4:
+            keep.pop(0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cb.cb_profile_enable(False)
+    kernels = {}
+    for name, kid in cb.KERNELS.items():
+        ms, n = cb.cb_profile_read(kid)
+        if n:
+            kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "total_ms": round(ms, 3)}
+    cb.cb_profile_reset()
+    T_total = int(sum(tokens[warm:warm + steps]))
+    dec_bytes = int(sum(alg_dec_bytes[warm:warm + steps]))
+    achieved = dec_bytes / (kernels["decode"]["total_ms"] * 1e-3) / 1e9
+    result = {
+        "metric": "ragged-attention tokens/s per step",
+        "value": round(T_total / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "scheduler-trace replay (500 steps, Poisson(8) arrivals, lognormal prompts, "
+                               "geometric outputs)", "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "token_budget": m, "num_blocks": wl.num_blocks, "seed": wl.seed,
+                   "tokens_timed": T_total},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
+                     "traffic": None},
+        "device_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
+        "kernels": kernels,
+    }
     print(json.dumps(result), flush=True)
     return 0
 
