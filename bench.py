@@ -108,6 +108,14 @@ def cpu_baseline(wl, step, budget_s=25.0):
             "sample": sample + ", fp64 numpy, one call per request incl. gathering inputs", "seconds": round(dt, 3)}
 
 
+def launch_step(cb, run, st, q, k_new, v_new, o, ws, stream):
+    """Append + attention of one built step through the single-call entry point."""
+    T = st.num_tokens
+    cb.cb_step_forward(run.shape, st.num_reqs, T, st.max_blocks_per_req, st.cu_q_lens, st.ctx_lens,
+                       st.block_tables, q[:T], k_new[:T], v_new[:T], run.k_cache, run.v_cache, run.wl.scale,
+                       o[:T], ws, ws.numel(), stream)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +125,9 @@ def main(argv=None):
                     help="2: mixed step (default), 3: decode-only GQA, 4: chunked prefill, "
                          "5: the 500-step scheduler trace (steps = trace steps after the warm-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--api", choices=["fused", "split"], default="fused",
+                    help="fused: one cb_step_forward call per step (one metadata upload); split: Batch upload + "
+                         "cb_kv_append + cb_ragged_attention")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
                          "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
@@ -160,7 +171,9 @@ def main(argv=None):
     alg = algorithmic(wl, step0)
     T = step0.num_tokens
     o = torch.empty_like(q)
-    ws_bytes = cb.cb_ragged_attention_workspace_size(run.shape, cb.Batch.from_step(step0).struct)
+    ws_bytes = max(cb.cb_ragged_attention_workspace_size(run.shape, cb.Batch.from_step(step0).struct),
+                   cb.cb_step_workspace_size(run.shape, step0.num_reqs, T, step0.max_blocks_per_req,
+                                             step0.cu_q_lens, step0.ctx_lens))
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -169,6 +182,12 @@ def main(argv=None):
     def one_step():
         t0 = time.perf_counter()
         s = base.clone()
+        if args.api == "fused":
+            st = s.build_raw()           # the library's own arrays, no copies
+            host_ms.append((time.perf_counter() - t0) * 1e3)
+            launch_step(cb, run, st, q, k_new, v_new, o, ws, stream)
+            s.commit()
+            return s
         st = s.build()
         batch = cb.Batch.from_step(st)
         host_ms.append((time.perf_counter() - t0) * 1e3)
@@ -237,7 +256,7 @@ def main(argv=None):
         "config": {"workload": names[args.config], "num_tokens": T, "num_reqs": step0.num_reqs,
                    "num_decode": step0.num_decode, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "token_budget": wl.token_budget,
-                   "seed": wl.seed},
+                   "seed": wl.seed, "api": args.api},
         "roofline": roof,
         "device_ms_per_step": round(device_ms, 4),
         "host_build_ms_per_step": round(float(np.mean(host_ms)), 4),
@@ -282,7 +301,9 @@ def bench_trace(args):
         st = dry.build()
         b = cb.cb_batch(st.num_reqs, st.num_tokens, st.max_blocks_per_req, 256, 256, 256,
                         st.cu_q_lens.ctypes.data, st.ctx_lens.ctypes.data)
-        need = max(need, cb.cb_ragged_attention_workspace_size(run.shape, b))
+        need = max(need, cb.cb_ragged_attention_workspace_size(run.shape, b),
+                   cb.cb_step_workspace_size(run.shape, st.num_reqs, st.num_tokens, st.max_blocks_per_req,
+                                             st.cu_q_lens, st.ctx_lens))
         alg = algorithmic(wl, st)
         alg_dec_bytes.append(alg["decode"]["bytes"])
         tokens.append(st.num_tokens)
@@ -295,9 +316,15 @@ def bench_trace(args):
     def one(kstep):
         for r in wl.arrivals[kstep]:
             sched.add(r.req_id, r.prompt_len, r.out_len)
+        if args.api == "fused":
+            st = sched.build_raw()
+            T = st.num_tokens
+            launch_step(cb, run, st, q, k_new, v_new, o, ws, stream)
+            sched.commit()
+            return None, T
         st = sched.build()
-        batch = cb.Batch.from_step(st)
         T = st.num_tokens
+        batch = cb.Batch.from_step(st)
         cb.cb_kv_append(run.shape, batch.struct, k_new, v_new, run.k_cache, run.v_cache, stream)
         cb.cb_ragged_attention(run.shape, batch.struct, q, run.k_cache, run.v_cache, wl.scale, o, ws, ws.numel(),
                                stream)
@@ -346,7 +373,7 @@ def bench_trace(args):
         "config": {"workload": "scheduler-trace replay (500 steps, Poisson(8) arrivals, lognormal prompts, "
                                "geometric outputs)", "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "token_budget": m, "num_blocks": wl.num_blocks, "seed": wl.seed,
-                   "tokens_timed": T_total},
+                   "tokens_timed": T_total, "api": args.api},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
                      "traffic": None},

@@ -122,6 +122,29 @@ int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void
                         const void* k_cache, const void* v_cache, float scale, void* o,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * One whole step from host metadata: KV append then ragged attention, with the metadata and
+ * the launch plan sent to the device in a single copy. This is the same work as uploading
+ * cu_q_lens / ctx_lens / block_tables, calling cb_kv_append and then cb_ragged_attention,
+ * with fewer device operations per step.
+ *   h_cu_q_lens [num_reqs+1], h_ctx_lens [num_reqs], h_block_tables [num_reqs *
+ *       max_blocks_per_req]  host int32, as in cb_batch and cb_step (the step builder's
+ *       arrays can be passed as they are). Every block id a row of the step touches must
+ *       lie in [0, num_blocks); this is checked on the host (CB_ERR_INVALID_ARG).
+ *   q, k_new, v_new, k_cache, v_cache, scale, o: as in cb_kv_append / cb_ragged_attention.
+ *   workspace: device, 256-byte aligned, at least cb_step_workspace_size() bytes; it holds
+ *       the step's metadata, plan and partials and must not be shared by calls in flight.
+ * ------------------------------------------------------------------------------------- */
+size_t cb_step_workspace_size(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
+                              int32_t max_blocks_per_req, const int32_t* h_cu_q_lens,
+                              const int32_t* h_ctx_lens);
+
+int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
+                    int32_t max_blocks_per_req, const int32_t* h_cu_q_lens,
+                    const int32_t* h_ctx_lens, const int32_t* h_block_tables, const void* q,
+                    const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message describing the last error on this thread ("" if none). Owned by the library. */
 const char* cb_last_error(void);
 

@@ -72,6 +72,10 @@ def _load():
         "cb_ragged_attention_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch)]),
         "cb_ragged_attention": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), P, P, P,
                                                ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "cb_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32, P, P]),
+        "cb_step_forward": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           P, P, P, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "cb_last_error": (ctypes.c_char_p, []),
         "cb_version": (ctypes.c_char_p, []),
         "cb_set_tuning": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
@@ -97,7 +101,8 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_attention", "cb_last_error",
+EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_attention", "cb_step_workspace_size",
+            "cb_step_forward", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_reset",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats")
@@ -146,6 +151,33 @@ def cb_ragged_attention(shape: cb_shape, batch: cb_batch, q, k_cache, v_cache, s
     return _check(lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(batch), _ptr(q), _ptr(k_cache),
                                           _ptr(v_cache), ctypes.c_float(scale), _ptr(o), _ptr(workspace),
                                           ctypes.c_size_t(workspace_bytes), _stream(stream)))
+
+
+def _host_i32(a):
+    """Host int32 data as (address, owner): a ctypes int32 pointer (a built step's own arrays,
+    passed through without a copy) or anything numpy turns into a contiguous int32 array."""
+    if isinstance(a, _i32p):
+        return ctypes.cast(a, ctypes.c_void_p).value, None
+    arr = np.ascontiguousarray(a, dtype=np.int32)
+    return arr.ctypes.data, arr
+
+
+def cb_step_workspace_size(shape: cb_shape, num_reqs: int, num_tokens: int, max_blocks_per_req: int, h_cu_q_lens,
+                           h_ctx_lens) -> int:
+    (cu, _a), (ctx, _b) = _host_i32(h_cu_q_lens), _host_i32(h_ctx_lens)
+    return int(lib.cb_step_workspace_size(ctypes.byref(shape), int(num_reqs), int(num_tokens), int(max_blocks_per_req),
+                                          cu, ctx))
+
+
+def cb_step_forward(shape: cb_shape, num_reqs: int, num_tokens: int, max_blocks_per_req: int, h_cu_q_lens,
+                    h_ctx_lens, h_block_tables, q, k_new, v_new, k_cache, v_cache, scale: float, o, workspace,
+                    workspace_bytes: int, stream=None) -> int:
+    """Host metadata may be numpy arrays or the int32 pointers of a cb_step (Scheduler.build_raw)."""
+    (cu, _a), (ctx, _b), (bt, _c) = _host_i32(h_cu_q_lens), _host_i32(h_ctx_lens), _host_i32(h_block_tables)
+    return _check(lib.cb_step_forward(ctypes.byref(shape), int(num_reqs), int(num_tokens), int(max_blocks_per_req),
+                                      cu, ctx, bt, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                      ctypes.c_float(scale), _ptr(o), _ptr(workspace),
+                                      ctypes.c_size_t(workspace_bytes), _stream(stream)))
 
 
 def cb_last_error() -> str:

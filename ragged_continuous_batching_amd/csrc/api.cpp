@@ -25,6 +25,7 @@ hipError_t launch_rows(const RowArgs& a, int elem_bytes, int head_dim, int group
 hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_rows_mfma(const RowArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_stage_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 namespace {
 
@@ -39,6 +40,7 @@ struct Tuning {
   int32_t prefill_touch = 0;      // 1: prefill pulls key tiles two steps ahead toward L2
   int32_t decode_group = 8;       // most query heads one decode wave handles (1, 2, 4 or 8)
   int32_t decode_mfma = 1;        // 1: grouped-query decode (4+ heads per kv head) on MFMA
+  int32_t stage_kernel = 1;       // 1: uploads run as a copy kernel on the stream; 0: copy engine
 };
 Tuning g_tuning;
 
@@ -50,6 +52,19 @@ struct ProfRec {
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;     // events of earlier records, reused (no create per launch)
+
+hipEvent_t pooled_event() {               // caller holds g_prof_mu
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  // timing only: no system-scope fence around the record, so the marker does not flush
+  // caches between the kernels it brackets (elapsed times are read after a device wait)
+  hipEvent_t e = nullptr;
+  return hipEventCreateWithFlags(&e, hipEventDisableSystemFence) == hipSuccess ? e : nullptr;
+}
 
 struct ProfScope {
   int kernel;
@@ -58,7 +73,11 @@ struct ProfScope {
   ProfScope(int k, hipStream_t s) : kernel(k), stream(s) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
-    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) {
+    start = pooled_event();
+    stop = pooled_event();
+    if (!start || !stop) {
+      if (start) g_event_pool.push_back(start);
+      if (stop) g_event_pool.push_back(stop);
       start = stop = nullptr;
       return;
     }
@@ -75,6 +94,7 @@ struct ProfScope {
 // ---- pinned staging ring for the plan upload -------------------------------------------
 struct Staging {
   void* host = nullptr;
+  void* host_dev = nullptr;     // the same pinned buffer as a device-side address
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool in_flight = false;
@@ -82,12 +102,18 @@ struct Staging {
 constexpr int kRing = 8;
 std::mutex g_ring_mu;
 Staging g_ring[kRing];
+std::vector<void*> g_ring_retired;
 int g_ring_next = 0;
 
-// Copies `bytes` from `src` to device `dst` on `stream` through pinned memory. The staging
-// slot is reused only after its previous copy has completed (event wait).
-int upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+// Copies `bytes` to device `dst` on `stream` through pinned memory: `fill(host)` writes the
+// bytes straight into a staging slot, so a call makes no host allocation once the slots have
+// grown to size (capacities are powers of two). A slot is reused only after its previous
+// copy has completed (event wait). With the stage kernel the copy moves `bytes` rounded up to
+// 16, so `dst` must have room for that.
+template <class Fill>
+int upload(void* dst, size_t bytes, hipStream_t stream, Fill&& fill) {
   if (bytes == 0) return CB_OK;
+  bytes = (bytes + 15) & ~static_cast<size_t>(15);
   std::lock_guard<std::mutex> lk(g_ring_mu);
   Staging& s = g_ring[g_ring_next];
   g_ring_next = (g_ring_next + 1) % kRing;
@@ -95,19 +121,27 @@ int upload(void* dst, const void* src, size_t bytes, hipStream_t stream) {
     if (hipEventSynchronize(s.ev) != hipSuccess) return fail(CB_ERR_HIP, "plan upload: event wait failed");
     s.in_flight = false;
   }
-  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
+  // the event only tells the host that the copy has finished reading the slot
+  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess)
     return fail(CB_ERR_HIP, "plan upload: hipEventCreate failed");
   if (s.cap < bytes) {
-    if (s.host) hipHostFree(s.host);
+    // A kernel may have read the old buffer directly: it is kept (not freed) until the
+    // process ends, which growth by powers of two bounds to the size of the last buffer.
+    if (s.host) g_ring_retired.push_back(s.host);
     s.host = nullptr;
     s.cap = 0;
-    size_t cap = std::max<size_t>(bytes, 1 << 16);
-    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess)
+    size_t cap = size_t{1} << 16;
+    while (cap < bytes) cap <<= 1;
+    // coherent: the device reads what the host wrote before the launch, never a cached copy
+    if (hipHostMalloc(&s.host, cap, hipHostMallocCoherent) != hipSuccess)
       return fail(CB_ERR_HIP, "plan upload: hipHostMalloc(%zu) failed", cap);
+    if (hipHostGetDevicePointer(&s.host_dev, s.host, 0) != hipSuccess)
+      return fail(CB_ERR_HIP, "plan upload: hipHostGetDevicePointer failed");
     s.cap = cap;
   }
-  std::memcpy(s.host, src, bytes);
-  hipError_t e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  fill(static_cast<char*>(s.host));
+  hipError_t e = g_tuning.stage_kernel ? launch_stage_copy(s.host_dev, dst, bytes, stream)
+                                       : hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail(CB_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
   if (hipEventRecord(s.ev, stream) != hipSuccess) return fail(CB_ERR_HIP, "plan upload: event record failed");
   s.in_flight = true;
@@ -322,6 +356,8 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.prefill_touch = value != 0;
   } else if (std::strcmp(key, "decode_mfma") == 0) {
     g_tuning.decode_mfma = value != 0;
+  } else if (std::strcmp(key, "stage_kernel") == 0) {
+    g_tuning.stage_kernel = value != 0;
   } else if (std::strcmp(key, "decode_group") == 0) {
     if (value != 1 && value != 2 && value != 4 && value != 8)
       return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: decode_group must be 1, 2, 4 or 8");
@@ -352,8 +388,8 @@ extern "C" int cb_profile_reset(void) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto& r : g_prof) {
     hipEventSynchronize(r.stop);
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
   }
   g_prof.clear();
   return CB_OK;
@@ -407,38 +443,17 @@ extern "C" size_t cb_ragged_attention_workspace_size(const cb_shape* shape, cons
   return p.total;
 }
 
-extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void* q,
-                                   const void* k_cache, const void* v_cache, float scale, void* o,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_shape(shape);
-  if (st) return st;
-  if ((st = check_batch(shape, batch))) return st;
-  if (batch->num_tokens == 0) return CB_OK;
-  if (!q || !k_cache || !v_cache || !o) return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: NULL tensor");
-  if (!(scale > 0.f) || !(scale < 3.0e38f))
-    return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: scale must be positive and finite");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(CB_ERR_INVALID_ARG, "cb_ragged_attention: tensors must be 16-byte aligned");
-  Plan p;
-  make_plan(shape, batch, p);
-  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
-    return fail(CB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, p.total);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(CB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+namespace cb {
+namespace {
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  std::vector<char> host(p.plan_bytes);
-  if (!p.splits.empty()) std::memcpy(host.data(), p.splits.data(), p.splits.size() * sizeof(RowSplit));
-  if (!p.combine.empty())
-    std::memcpy(host.data() + p.off_combine, p.combine.data(), p.combine.size() * sizeof(CombineRow));
-  if (!p.prefill.empty())
-    std::memcpy(host.data() + p.off_prefill, p.prefill.data(), p.prefill.size() * sizeof(PrefillItem));
-  if ((st = upload(ws, host.data(), p.plan_bytes, s))) return st;
-
+// Launches the attention kernels of plan `p`, whose work lists are already in the workspace
+// at `ws` (plan offsets are relative to `ws`). `batch` holds device metadata pointers.
+int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p, char* ws, const void* q,
+                     const void* k_cache, const void* v_cache, float scale, void* o, hipStream_t s) {
   const int eb = elem_bytes(shape);
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
   hipError_t e = hipSuccess;
+  int st = CB_OK;
   // Prefill tiles (MFMA-bound) and decode rows (HBM-bound) touch disjoint rows of O. With
   // "overlap_prefill" set, the prefill kernel runs on a side stream forked from `stream` and
   // joined back before the call returns, so the two can share the device. It is off by
@@ -485,4 +500,132 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_ragged_attention: launch failed: %s", hipGetErrorString(e));
   return CB_OK;
+}
+
+// Serialises the plan's work lists at their offsets into `out` (plan_bytes long).
+void write_plan(const Plan& p, char* out) {
+  if (!p.splits.empty()) std::memcpy(out, p.splits.data(), p.splits.size() * sizeof(RowSplit));
+  if (!p.combine.empty()) std::memcpy(out + p.off_combine, p.combine.data(), p.combine.size() * sizeof(CombineRow));
+  if (!p.prefill.empty())
+    std::memcpy(out + p.off_prefill, p.prefill.data(), p.prefill.size() * sizeof(PrefillItem));
+}
+
+int check_tensors(const void* q, const void* k_cache, const void* v_cache, void* o, float scale, const char* fn) {
+  if (!q || !k_cache || !v_cache || !o) return fail(CB_ERR_INVALID_ARG, "%s: NULL tensor", fn);
+  if (!(scale > 0.f) || !(scale < 3.0e38f)) return fail(CB_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(CB_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return CB_OK;
+}
+
+// Workspace layout of cb_step_forward: the step metadata (cu_q_lens, ctx_lens,
+// block_tables), then the attention plan and partials at `plan_base`.
+struct StepLayout {
+  size_t off_cu = 0, off_ctx = 0, off_bt = 0, meta_bytes = 0, plan_base = 0;
+};
+
+StepLayout step_layout(int32_t R, int32_t maxb) {
+  StepLayout l;
+  l.off_cu = 0;
+  l.off_ctx = static_cast<size_t>(R + 1) * 4;
+  l.off_bt = l.off_ctx + static_cast<size_t>(R) * 4;
+  l.meta_bytes = l.off_bt + static_cast<size_t>(R) * maxb * 4;
+  l.plan_base = align256(l.meta_bytes);
+  return l;
+}
+
+}  // namespace
+}  // namespace cb
+
+extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void* q,
+                                   const void* k_cache, const void* v_cache, float scale, void* o,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_batch(shape, batch))) return st;
+  if (batch->num_tokens == 0) return CB_OK;
+  if ((st = check_tensors(q, k_cache, v_cache, o, scale, "cb_ragged_attention"))) return st;
+  Plan p;
+  make_plan(shape, batch, p);
+  if (workspace_bytes < p.total || (p.total > 0 && !workspace))
+    return fail(CB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, p.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(CB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if ((st = upload(ws, p.plan_bytes, s, [&](char* host) { write_plan(p, host); }))) return st;
+  return launch_attention(shape, batch, p, ws, q, k_cache, v_cache, scale, o, s);
+}
+
+// A cb_batch over host metadata whose device pointers point into the step workspace.
+static cb_batch step_batch(int32_t R, int32_t T, int32_t maxb, const int32_t* h_cu, const int32_t* h_ctx,
+                           char* ws, const StepLayout& l) {
+  // a non-null placeholder lets the host-side checks run before the workspace is known
+  char* base = ws ? ws : reinterpret_cast<char*>(uintptr_t{256});
+  return cb_batch{R, T, maxb, reinterpret_cast<const int32_t*>(base + l.off_cu),
+                  reinterpret_cast<const int32_t*>(base + l.off_ctx), reinterpret_cast<const int32_t*>(base + l.off_bt),
+                  h_cu, h_ctx};
+}
+
+extern "C" size_t cb_step_workspace_size(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
+                                         int32_t max_blocks_per_req, const int32_t* h_cu_q_lens,
+                                         const int32_t* h_ctx_lens) {
+  if (check_shape(shape) || num_reqs < 0 || max_blocks_per_req < 0) return 0;
+  const StepLayout l = step_layout(num_reqs, max_blocks_per_req);
+  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr, l);
+  if (check_batch(shape, &b) || num_tokens == 0) return 0;
+  Plan p;
+  make_plan(shape, &b, p);
+  return l.plan_base + p.total;
+}
+
+extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens, int32_t max_blocks_per_req,
+                               const int32_t* h_cu_q_lens, const int32_t* h_ctx_lens, const int32_t* h_block_tables,
+                               const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               float scale, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (num_reqs < 0 || max_blocks_per_req < 0) return fail(CB_ERR_INVALID_ARG, "cb_step_forward: negative count");
+  const StepLayout l = step_layout(num_reqs, max_blocks_per_req);
+  char* ws = static_cast<char*>(workspace);
+  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, ws, l);
+  if ((st = check_batch(shape, &b))) return st;
+  if (num_tokens == 0) return CB_OK;
+  if (!h_block_tables) return fail(CB_ERR_INVALID_ARG, "cb_step_forward: block tables are required");
+  for (int32_t r = 0; r < num_reqs; ++r) {            // every block a step row can touch
+    const int32_t nb = ceil_div(static_cast<int64_t>(h_ctx_lens[r]) + h_cu_q_lens[r + 1] - h_cu_q_lens[r], kBlockSize);
+    const int32_t* row = h_block_tables + static_cast<size_t>(r) * max_blocks_per_req;
+    for (int32_t j = 0; j < nb && h_cu_q_lens[r + 1] > h_cu_q_lens[r]; ++j)
+      if (row[j] < 0 || row[j] >= shape->num_blocks)
+        return fail(CB_ERR_INVALID_ARG, "cb_step_forward: block id %d of request %d out of range", row[j], r);
+  }
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))
+    return fail(CB_ERR_INVALID_ARG, "cb_step_forward: new K/V must be non-NULL and 16-byte aligned");
+  if ((st = check_tensors(q, k_cache, v_cache, o, scale, "cb_step_forward"))) return st;
+  Plan p;
+  make_plan(shape, &b, p);
+  if (!ws || workspace_bytes < l.plan_base + p.total)
+    return fail(CB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                l.plan_base + p.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  // one upload: metadata, then the plan
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = upload(ws, l.plan_base + p.plan_bytes, s, [&](char* host) {
+    std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
+    std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
+    std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
+    write_plan(p, host + l.plan_base);
+  });
+  if (st) return st;
+
+  AppendArgs aa{k_new, v_new, k_cache, v_cache, b.cu_q_lens, b.ctx_lens, b.block_tables, num_reqs, num_tokens,
+                max_blocks_per_req, shape->num_kv_heads, shape->num_blocks};
+  hipError_t e;
+  {
+    ProfScope prof(CB_KERNEL_APPEND, s);
+    e = launch_kv_append(aa, elem_bytes(shape), shape->head_dim, s);
+  }
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_step_forward: append launch failed: %s", hipGetErrorString(e));
+  return launch_attention(shape, &b, p, ws + l.plan_base, q, k_cache, v_cache, scale, o, s);
 }

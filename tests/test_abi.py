@@ -133,3 +133,31 @@ def test_kv_bytes_per_position_matches_pages():
     shape = cb.make_shape(32, 32, 128, 1, "bf16")
     per_block_bytes = 2 * shape.num_kv_heads * shape.block_size * shape.head_dim * 2
     assert per_block_bytes // shape.block_size == 16384
+
+
+def test_step_forward_checks_host_metadata():
+    shape = _shape(num_blocks=8)
+    cu = np.array([0, 3], np.int32)
+    ctx = np.array([14], np.int32)
+    bt = np.array([[0, 9]], np.int32)                       # block 9 is outside the pool of 8
+    need = cb.cb_step_workspace_size(shape, 1, 3, 2, cu, ctx)
+    assert need > 0
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_step_forward(shape, 1, 3, 2, cu, ctx, bt, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, need, 0)
+    assert e.value.status == cb.CB_ERR_INVALID_ARG and "out of range" in str(e.value)
+    bt = np.array([[0, 1]], np.int32)
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_step_forward(shape, 1, 3, 2, cu, ctx, bt, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, need - 1, 0)
+    assert e.value.status == cb.CB_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_step_forward(shape, 1, 3, 2, cu, ctx, bt, FAKE, FAKE, FAKE, FAKE, FAKE, -1.0, FAKE, FAKE, need, 0)
+    assert e.value.status == cb.CB_ERR_INVALID_ARG and "scale" in str(e.value)
+
+
+def test_scale_must_be_positive():
+    shape = _shape()
+    b = _batch([0, 1], [3], 1)
+    for sc in (0.0, -0.5, float("inf"), float("nan")):
+        rc = cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, sc, FAKE, FAKE,
+                                        1 << 30, None)
+        assert rc == cb.CB_ERR_INVALID_ARG, sc

@@ -150,6 +150,66 @@ def test_append_is_bit_exact_and_stays_in_its_slots():
     assert torch.isnan(kc.permute(0, 2, 1, 3)[~written]).all()
 
 
+def step_forward(run, step, q, k, v):
+    """The fused entry point: one upload of host metadata + plan, append, attention."""
+    need = cb.cb_step_workspace_size(run.shape, step.num_reqs, step.num_tokens, step.max_blocks_per_req,
+                                     step.cu_q_lens, step.ctx_lens)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    cb.cb_step_forward(run.shape, step.num_reqs, step.num_tokens, step.max_blocks_per_req, step.cu_q_lens,
+                       step.ctx_lens, step.block_tables, q, k, v, run.k_cache, run.v_cache, run.wl.scale, o, ws,
+                       need, run.stream)
+    return o
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,dtype", [("mixed", 8, 2, 128, "bf16"), ("tile_edges", 4, 4, 128, "bf16"),
+                                                 ("long_decode", 16, 2, 128, "bf16"), ("mixed", 2, 2, 64, "f32")])
+def test_step_forward_matches_two_calls_and_oracle(name, hq, hkv, d, dtype):
+    wl = small_workload(name, hq, hkv, d, dtype)
+    run, step, batch, o = run_one_step(wl)           # append + attention through the two calls
+    q, k, v = run.step_inputs(step)
+    o2 = step_forward(run, step, q, k, v)            # appends the same rows again, then attends
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o)
+    check(o2, oracle_full(wl, step), dtype, f"step_forward {name} Hq={hq} Hkv={hkv} D={d} {dtype}")
+
+
+def test_copy_engine_and_stage_kernel_uploads_agree():
+    """The metadata upload as a copy kernel (default) or through the copy engine: same bits."""
+    wl = small_workload("mixed", 8, 2, 128, "bf16")
+    outs = []
+    try:
+        for mode in (0, 1, 0):
+            cb.cb_set_tuning("stage_kernel", mode)
+            run = DeviceRun(wl)
+            step = run.sched.build()
+            run.write_history(step)
+            q, k, v = run.step_inputs(step)
+            outs.append(step_forward(run, step, q, k, v))
+            outs.append(run.attention(cb.Batch.from_step(step, device=run.device), q))
+    finally:
+        cb.cb_set_tuning("stage_kernel", 1)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    check(outs[0], oracle_full(wl, step), "bf16", "uploads")
+
+
+def test_step_forward_fresh_cache_config2():
+    """Config 2 through the fused entry point alone (history appended beforehand)."""
+    wl = W.config(2, value_reading="unit")
+    run = DeviceRun(wl)
+    step = run.sched.build()
+    run.write_history(step)
+    q, k, v = run.step_inputs(step)
+    o = step_forward(run, step, q, k, v)
+    torch.cuda.synchronize()
+    rows = list(range(step.num_decode)) + [t for t in sample_rows(step, 16, np.random.default_rng(9))
+                                           if t >= step.num_decode]
+    rows, ref = oracle_rows(wl, step, rows)
+    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "step_forward config 2")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (32, 2)])
 def test_gqa_decode_vector_alu_kernel(hq, hkv):
     """The vector-ALU decode kernel also serves grouped-query rows when the matrix-core
