@@ -23,7 +23,7 @@ std::string& last_error() {
 hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int head_dim, hipStream_t s);
 hipError_t launch_rows(const RowArgs& a, int elem_bytes, int head_dim, int group, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int waves, hipStream_t s);
 hipError_t launch_rows_mfma(const RowArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_stage_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
@@ -41,6 +41,8 @@ struct Tuning {
   int32_t decode_group = 8;       // most query heads one decode wave handles (1, 2, 4 or 8)
   int32_t decode_mfma = 1;        // 1: grouped-query decode (4+ heads per kv head) on MFMA
   int32_t stage_kernel = 1;       // 1: uploads run as a copy kernel on the stream; 0: copy engine
+  int32_t prefill_waves = 0;      // waves per prefill work-group: 4, 8 (32 query rows each) or
+                                  // 0 = 8 when that still gives two work-groups per CU, else 4
 };
 Tuning g_tuning;
 
@@ -232,6 +234,7 @@ struct Plan {
   int32_t n_parts = 0;
   int group = 1;         // query heads per decode wave
   bool mfma_decode = false;  // decode rows on the MFMA kernel
+  int prefill_waves = 4;     // waves (x 32 query rows) per prefill work-group
   int n_sub = 1;         // decode waves per kv head
   size_t off_combine = 0, off_prefill = 0, plan_bytes = 0, off_part_o = 0, off_part_ml = 0, total = 0;
 };
@@ -249,6 +252,17 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
   }
   p.n_sub = q_per_kv / p.group;
   const bool mfma_prefill = s->dtype == CB_BF16;
+  p.prefill_waves = g_tuning.prefill_waves;
+  if (p.prefill_waves == 0) {
+    // 256-row work-groups read each key/value tile once for twice the rows, but a CU holds
+    // only one of them (registers); take them when there are enough to fill every CU twice
+    int64_t items256 = 0;
+    for (int32_t r = 0; r < b->num_reqs; ++r) {
+      const int32_t q = b->h_cu_q_lens[r + 1] - b->h_cu_q_lens[r];
+      if (q > 1 && mfma_prefill) items256 += ceil_div(q, 256) * static_cast<int64_t>(s->num_q_heads);
+    }
+    p.prefill_waves = items256 >= 2 * kNumCUs ? 8 : 4;
+  }
 
   // rows that take the split-K path, longest first
   struct Row { int32_t token, req, kv_len; };
@@ -267,12 +281,13 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
     } else {
       // one group per (request, kv head): all its q-tiles and query heads read the same
       // key/value tiles, so they are kept on one XCD (shared L2) and run side by side
-      const int32_t n_qt = ceil_div(q, kPrefillRows);
+      const int32_t rows = 32 * p.prefill_waves;
+      const int32_t n_qt = ceil_div(q, rows);
       for (int32_t g = 0; g < s->num_kv_heads; ++g) {
         PrefillGroup grp;
         for (int32_t qt = n_qt - 1; qt >= 0; --qt) {
-          const int32_t qb = qt * kPrefillRows;
-          const int32_t tiles = ceil_div(c + std::min(qb + kPrefillRows, q), kPrefillKeys);
+          const int32_t qb = qt * rows;
+          const int32_t tiles = ceil_div(c + std::min(qb + rows, q), kPrefillKeys);
           for (int32_t hh = 0; hh < q_per_kv; ++hh) {
             grp.items.push_back({r, qb, g * q_per_kv + hh, tiles});
             grp.cost += tiles;
@@ -356,6 +371,10 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.prefill_touch = value != 0;
   } else if (std::strcmp(key, "decode_mfma") == 0) {
     g_tuning.decode_mfma = value != 0;
+  } else if (std::strcmp(key, "prefill_waves") == 0) {
+    if (value != 0 && value != 4 && value != 8)
+      return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: prefill_waves must be 0, 4 or 8");
+    g_tuning.prefill_waves = value;
   } else if (std::strcmp(key, "stage_kernel") == 0) {
     g_tuning.stage_kernel = value != 0;
   } else if (std::strcmp(key, "decode_group") == 0) {
@@ -474,7 +493,7 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
                    shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2,
                    g_tuning.prefill_touch};
     ProfScope prof(CB_KERNEL_PREFILL, ps);
-    e = launch_prefill(pa, shape->head_dim, ps);
+    e = launch_prefill(pa, shape->head_dim, p.prefill_waves, ps);
   }
   if (e == hipSuccess && !p.splits.empty()) {
     RowArgs ra{q, k_cache, v_cache, o,

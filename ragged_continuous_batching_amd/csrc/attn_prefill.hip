@@ -7,9 +7,9 @@
 // masked pairs are not computed at all, and the cache is read one block at a time into a
 // running online-softmax state.
 //
-// One work-group (4 waves) = 128 query rows of one request and one query head. Each wave
-// owns 32 rows. Keys stream through LDS in tiles of 64 (4 cache blocks), double-buffered:
-// one barrier per tile, and the next tile's global loads overlap the current tile's math.
+// One work-group (4 or 8 waves) = 128 or 256 query rows of one request and one query head.
+// Each wave owns 32 rows. Keys stream through LDS in tiles of 64 (4 cache blocks),
+// double-buffered, and the global loads of later tiles overlap the current tile's math.
 // The products are computed transposed so that the query index stays the lane index:
 //   S^T[key][q] = K Q^T      A = K tile rows from LDS, B = the wave's Q rows (registers)
 //   O^T[d][q]  += V^T P^T    A = V^T rows from LDS (the cache stores V transposed),
@@ -44,9 +44,11 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a) {
   using Geo = PrefillGeom<D>;
+  constexpr int NT = 64 * NW;                           // threads
+  constexpr int ROWS = 32 * NW;                         // query rows of the work-group
   constexpr int KS = Geo::KS, VS = Geo::VS, DCH = Geo::DCH, DT = Geo::DT;
   __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
   __shared__ int32_t lds_bt[kPrefillLdsBlocks];   // block ids of the keys this WG reads
@@ -67,14 +69,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int qrow = wave_row0 + col;                           // this lane's row in the request
   const bool wave_active = wave_row0 < nq;
   const int wave_keys = c + min(wave_row0 + 31, nq - 1) + 1;  // keys any row of the wave sees
-  const int wg_keys = c + min(it.q_begin + kPrefillRows - 1, nq - 1) + 1;
+  const int wg_keys = c + min(it.q_begin + ROWS - 1, nq - 1) + 1;
   const int n_tiles = (wg_keys + kPrefillKeys - 1) / kPrefillKeys;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
   // Stage the block ids once, so that each tile's loads depend on an LDS read rather than
   // on a global load. Keys past kPrefillLdsBlocks*16 read the global table instead (a
   // uniform per-tile branch).
   const int n_bt = min((wg_keys + kBlockSize - 1) / kBlockSize, kPrefillLdsBlocks);
-  for (int i = threadIdx.x; i < n_bt; i += 256) {
+  for (int i = threadIdx.x; i < n_bt; i += NT) {
     const int blk = bt[i];
     lds_bt[i] = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
   }
@@ -102,10 +104,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // pages); at D = 64 the two halves of the work-group take two pages per load. Only the
   // tile that reaches wg_keys (the last key any row of this work-group sees) clamps pages
   // and zeroes positions past it.
-  constexpr int PPL = 128 / D;                                     // pages per load
+  constexpr int TPP = 2 * D;                                       // threads per page (16 B each)
+  constexpr int PPL = NT / TPP;                                    // pages per load
   constexpr int NL = 4 / PPL;                                      // loads per tile
+  static_assert(NL * PPL == 4, "a tile is 4 pages");
   u32x4 kreg[NL], vreg[NL];
-  const int tl = tid % (256 / PPL);                                // thread within its page
+  const int tl = tid % TPP;                                        // thread within its page
   auto page_block = [&](int pidx) -> int {                         // block id of key page pidx
     const int i = min(pidx, (wg_keys - 1) / kBlockSize);
     int blk;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   auto load_tile = [&](int j) {
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int page = u * PPL + tid / (256 / PPL);                // wave-uniform
+      const int page = u * PPL + tid / TPP;                // wave-uniform
       const int64_t base = (static_cast<int64_t>(page_block(j * 4 + page)) * hkv + g) * page_elems;
       kreg[u] = *reinterpret_cast<const u32x4*>(kc + base + (tl / (D / 8)) * D + (tl % (D / 8)) * 8);
       vreg[u] = *reinterpret_cast<const u32x4*>(vc + base + tl * 8);
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if ((j + 1) * kPrefillKeys > wg_keys) {        // the last tile: zero keys >= wg_keys
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const int page = u * PPL + tid / (256 / PPL);
+        const int page = u * PPL + tid / TPP;
         const int kpos = j * kPrefillKeys + page * kBlockSize + tl / (D / 8);
         if (kpos >= wg_keys) kreg[u] = u32x4{0u, 0u, 0u, 0u};
         const int vpos = j * kPrefillKeys + page * kBlockSize + (tl % 2) * 8;
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int page = u * PPL + tid / (256 / PPL);
+      const int page = u * PPL + tid / TPP;
       *reinterpret_cast<u32x4*>(kl + (page * kBlockSize + tl / (D / 8)) * KS + (tl % (D / 8)) * 8) = kreg[u];
       // Inside each 16-key page, key k sits at position (k&3) + 4*(k>>3) + 8*((k>>2)&1):
       // positions 0..7 then hold keys 0-3 and 8-11, positions 8..15 keys 4-7 and 12-15, the
@@ -282,6 +286,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   __syncthreads();
   // Per tile j: step (reads buffer j&1, scores of j+1 from the other buffer), a barrier
   // (buffer j&1 is free), tile j+2 from registers into it, the loads of j+3, a barrier.
+  // (A variant with separate key and value buffer rings and one barrier per tile measured
+  // slower: the first barrier keeps the waves of the work-group in step.)
   auto advance = [&](int j) {
     __syncthreads();
     if (j + 2 < n_tiles) {
@@ -316,12 +322,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s) {
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int waves, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(a.n_items), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(a.n_items), dim3(256), 0, s, a);
+  if (waves == 8) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((prefill_kernel<128, 8>), dim3(a.n_items), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<64, 8>), dim3(a.n_items), dim3(512), 0, s, a);
+  } else {
+    if (head_dim == 128)
+      hipLaunchKernelGGL((prefill_kernel<128, 4>), dim3(a.n_items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<64, 4>), dim3(a.n_items), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

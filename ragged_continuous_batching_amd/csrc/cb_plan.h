@@ -27,8 +27,8 @@ struct CombineRow {
   int32_t pad;
 };
 
-// One tile of a prefill chunk: rows q_begin .. q_begin+kPrefillRows-1 of request `req`
-// (clipped to its row count), query head `head`. req < 0 marks an empty slot.
+// One tile of a prefill chunk: rows q_begin .. q_begin+R-1 of request `req` (R = 32 x the
+// work-group's waves, clipped to its row count), query head `head`. req < 0 marks an empty slot.
 struct PrefillItem {
   int32_t req;
   int32_t q_begin;
@@ -37,10 +37,10 @@ struct PrefillItem {
 };
 
 constexpr int kBlockSize = 16;         // KV positions per physical block
-constexpr int kPrefillRows = 128;      // query rows per prefill work-group (4 waves x 32)
 constexpr int kPrefillKeys = 64;       // keys per prefill K/V tile (4 blocks)
 constexpr int kPrefillLdsBlocks = 2048;  // block ids a prefill work-group stages in LDS
 constexpr int kMaxSplitBlocks = 64;    // blocks per decode split (one block id per lane)
+constexpr int kNumCUs = 256;           // compute units of the target GPU (MI355X)
 
 struct AppendArgs {
   const void* k_new;

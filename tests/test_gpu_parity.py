@@ -210,6 +210,31 @@ def test_step_forward_fresh_cache_config2():
     check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "step_forward config 2")
 
 
+@pytest.mark.parametrize("name,hq,hkv,d", [("mixed", 8, 2, 128), ("tile_edges", 4, 4, 128), ("mixed", 4, 2, 64)])
+def test_prefill_eight_wave_work_groups(name, hq, hkv, d):
+    """256 query rows per prefill work-group (8 waves) against the oracle."""
+    wl = small_workload(name, hq, hkv, d, "bf16")
+    try:
+        cb.cb_set_tuning("prefill_waves", 8)
+        run, step, batch, o = run_one_step(wl)
+    finally:
+        cb.cb_set_tuning("prefill_waves", 0)
+    check(o, oracle_full(wl, step), "bf16", f"prefill 8 waves {name} Hq={hq} Hkv={hkv} D={d}")
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+def test_config4_prefill_waves(waves):
+    """Config 4 with each prefill work-group size forced (the default picks one by size)."""
+    wl = W.config(4)
+    try:
+        cb.cb_set_tuning("prefill_waves", waves)
+        run, step, batch, o = run_one_step(wl)
+    finally:
+        cb.cb_set_tuning("prefill_waves", 0)
+    rows, ref = oracle_rows(wl, step, sample_rows(step, 20, np.random.default_rng(4)) + [255, 256, 257, 511, 512])
+    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", f"config 4, {waves}-wave prefill")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (32, 2)])
 def test_gqa_decode_vector_alu_kernel(hq, hkv):
     """The vector-ALU decode kernel also serves grouped-query rows when the matrix-core
