@@ -60,14 +60,17 @@ def source_sha(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"decode": ("attn_rows.hip", "cb_device.h", "cb_plan.h"),
-                  "prefill": ("attn_prefill.hip", "cb_device.h", "cb_plan.h")}
+KERNEL_SOURCES = {"row_attn_kernel": ("attn_rows.hip", "cb_device.h", "cb_plan.h"),
+                  "row_attn_mfma_kernel": ("attn_decode_gqa.hip", "cb_device.h", "cb_plan.h"),
+                  "prefill_kernel": ("attn_prefill.hip", "cb_device.h", "cb_plan.h")}
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, or None if stale/absent."""
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_pmc.json, or None if it is absent or the kernel's sources
+    have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
-    if not os.path.exists(path):
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
@@ -238,7 +241,7 @@ def main(argv=None):
     roof["kernel"] = cb.cb_kernel_name(cb.KERNELS[dominant])
     if dominant == "decode" and wl.dtype == "bf16" and wl.num_q_heads // wl.num_kv_heads >= 4:
         roof["kernel"] = "row_attn_mfma_kernel"        # grouped-query decode runs on the matrix cores
-    roof["traffic"] = measured_traffic(dominant, f"config{args.config}")
+    roof["traffic"] = measured_traffic(roof["kernel"], f"config{args.config}")
 
     result = {
         "metric": "ragged-attention tokens/s per step",

@@ -166,6 +166,12 @@ const char* cb_version(void);
  *   "decode_group"   most query heads of one kv head that a decode wave handles (1, 2, 4
  *                    or 8; default 8). Smaller groups use fewer registers per wave; the
  *                    waves of one kv head then read the same pages back to back.
+ *   "stage_kernel"   1 (default) = metadata and work lists are copied into the workspace by
+ *                    a kernel that reads the pinned staging buffer (same queue as the
+ *                    attention kernels); 0 = by the copy engine (hipMemcpyAsync)
+ *   "prefill_waves"  waves per bf16 prefill work-group: 4 (128 query rows, two work-groups
+ *                    per CU), 8 (256 rows, one per CU), or 0 (default) = 8 when a step has at
+ *                    least 2 x 256 such work-groups, else 4
  * Returns CB_ERR_INVALID_ARG for an unknown key or a negative value. */
 int cb_set_tuning(const char* key, int32_t value);
 
