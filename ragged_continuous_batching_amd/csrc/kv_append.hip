@@ -7,12 +7,13 @@
 //
 // Layout (include/cb.h): K pages are [block_size][D], V pages are [D][block_size] (V is
 // stored transposed). A work-group takes 16 consecutive packed rows and up to 4 kv heads:
-//   1. the first 16 threads find each row's request, block and slot;
-//   2. K rows are copied chunk by chunk (16 bytes per thread, key rows stay contiguous);
-//      V rows are staged in LDS;
-//   3. V elements leave LDS with 16 consecutive lanes on 16 consecutive rows of one d-row,
-//      so the rows of a prefill chunk that share a block land as one contiguous run of the
-//      transposed page (a decode row writes one element per d-row, as the layout implies).
+//   1. every thread loads its 16-byte chunks of the new K and V rows, while the first 16
+//      threads find each row's request, block and slot;
+//   2. K chunks go straight to their slots (key rows stay contiguous); V rows are staged in
+//      LDS;
+//   3. V^T leaves LDS per d-row: a group of 16/ES rows that occupies consecutive, aligned
+//      slots of one block (rows of a prefill chunk) is written as one 16-byte store; other
+//      rows (decode rows, the edges of a chunk) element by element, as the layout implies.
 #include <type_traits>
 
 #include "cb_device.h"
@@ -28,12 +29,30 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   using E = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
   __shared__ __align__(16) E vt[HEADS * ROWS * LS];
   __shared__ int32_t info_blk[ROWS], info_off[ROWS];
+  __shared__ int32_t info_run[ROWS / VEC];
 
   const int t0 = blockIdx.x * ROWS;
   const int g0 = blockIdx.y * HEADS;
   const int tid = threadIdx.x;
   const int nrows = min(ROWS, a.num_tokens - t0);
   const int nheads = min(HEADS, a.num_kv_heads - g0);
+  // The new K and V chunks of the work-group are requested first; the slot lookup (a binary
+  // search over cu_q_lens, then ctx_lens and the block table: a chain of dependent loads)
+  // runs while they are in flight.
+  constexpr int NPT = HEADS * ROWS * CH / 256;   // chunks per thread
+  static_assert(NPT * 256 == HEADS * ROWS * CH, "chunks must split evenly over 256 threads");
+  u32x4 kv[NPT], vv[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int e = tid + u * 256;
+    const int c = e % CH, row = (e / CH) % ROWS, hh = e / (CH * ROWS);
+    kv[u] = vv[u] = u32x4{0u, 0u, 0u, 0u};
+    if (row < nrows && hh < nheads) {
+      const int64_t src = ((static_cast<int64_t>(t0 + row) * a.num_kv_heads + g0 + hh) * D + c * VEC) * ES;
+      vv[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_new) + src);
+      kv[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k_new) + src);
+    }
+  }
   if (tid < ROWS) {
     int blk = -1, off = 0;
     if (tid < nrows) {
@@ -47,32 +66,61 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     info_blk[tid] = blk;
     info_off[tid] = off;
   }
+  // V rows into LDS
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int e = tid + u * 256;
+    const int c = e % CH, row = (e / CH) % ROWS, hh = e / (CH * ROWS);
+    if (row < nrows && hh < nheads) *reinterpret_cast<u32x4*>(&vt[(hh * ROWS + row) * LS + c * VEC]) = vv[u];
+  }
   __syncthreads();
-
-  // K rows straight to their slots; V rows into LDS
-  for (int e = tid; e < HEADS * ROWS * CH; e += 256) {
+  if (tid < ROWS / VEC) {                       // does row group tid fill one aligned run?
+    const int r0 = tid * VEC;
+    bool run = r0 + VEC <= nrows && info_blk[r0] >= 0 && info_off[r0] % VEC == 0;
+    for (int i = 1; i < VEC && run; ++i)
+      run = info_blk[r0 + i] == info_blk[r0] && info_off[r0 + i] == info_off[r0] + i;
+    info_run[tid] = run;
+  }
+  // K rows straight to their slots
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int e = tid + u * 256;
     const int c = e % CH, row = (e / CH) % ROWS, hh = e / (CH * ROWS);
     if (row >= nrows || hh >= nheads) continue;
-    const int64_t src = ((static_cast<int64_t>(t0 + row) * a.num_kv_heads + g0 + hh) * D + c * VEC) * ES;
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_new) + src);
-    *reinterpret_cast<u32x4*>(&vt[(hh * ROWS + row) * LS + c * VEC]) = vv;
     const int blk = info_blk[row];
     if (blk < 0) continue;
-    const u32x4 kv = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k_new) + src);
     const int64_t page = static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh;
     *reinterpret_cast<u32x4*>(static_cast<char*>(a.k_cache) +
-                              ((page * kBlockSize + info_off[row]) * D + c * VEC) * ES) = kv;
+                              ((page * kBlockSize + info_off[row]) * D + c * VEC) * ES) = kv[u];
   }
   __syncthreads();
 
-  // V^T: lane-consecutive rows within one d-row
-  for (int e = tid; e < HEADS * D * ROWS; e += 256) {
-    const int row = e % ROWS, d = (e / ROWS) % D, hh = e / (ROWS * D);
-    if (row >= nrows || hh >= nheads) continue;
-    const int blk = info_blk[row];
-    if (blk < 0) continue;
-    const int64_t page = static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh;
-    static_cast<E*>(a.v_cache)[(page * D + d) * kBlockSize + info_off[row]] = vt[(hh * ROWS + row) * LS + d];
+  // V^T: a group of VEC rows that fill VEC consecutive, aligned slots of one block (the rows
+  // of a prefill chunk, as a rule) leaves as one 16-byte store per d-row; other groups (decode
+  // rows, chunk edges) store element by element.
+  constexpr int GROUPS = ROWS / VEC;
+  for (int e = tid; e < HEADS * D * GROUPS; e += 256) {
+    const int grp = e % GROUPS, d = (e / GROUPS) % D, hh = e / (GROUPS * D);
+    if (hh >= nheads) continue;
+    const int r0 = grp * VEC;
+    if (r0 >= nrows) continue;
+    const E* src = &vt[(hh * ROWS + r0) * LS + d];
+    if (info_run[grp]) {
+      const int64_t page = static_cast<int64_t>(info_blk[r0]) * a.num_kv_heads + g0 + hh;
+      E vals[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) vals[i] = src[i * LS];
+      u32x4 w;
+      __builtin_memcpy(&w, vals, 16);
+      *reinterpret_cast<u32x4*>(static_cast<E*>(a.v_cache) + (page * D + d) * kBlockSize + info_off[r0]) = w;
+    } else {
+      for (int i = 0; i < VEC && r0 + i < nrows; ++i) {
+        const int blk = info_blk[r0 + i];
+        if (blk < 0) continue;
+        const int64_t page = static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh;
+        static_cast<E*>(a.v_cache)[(page * D + d) * kBlockSize + info_off[r0 + i]] = src[i * LS];
+      }
+    }
   }
 }
 
