@@ -153,7 +153,9 @@ const char* cb_version(void);
 
 /* Tuning knobs (process-wide, host-side). Keys:
  *   "split_blocks"   KV blocks per split of a decode row, at most 64; 0 = automatic (default)
- *   "target_waves"   automatic split sizing aims for at least this many wave items
+ *   "target_waves"   automatic split sizing aims for at least this many wave items; 0
+ *                    (default) = 8192 for the vector-ALU decode kernel, 4096 for the
+ *                    matrix-core one
  *   "overlap_prefill" 1 = run prefill tiles on an internal side stream (forked from and
  *                    joined back to `stream`) concurrently with decode rows; 0 (default)
  *                    runs them one after the other on `stream`

@@ -34,7 +34,7 @@ constexpr double kLog2e = 1.4426950408889634;
 // ---- tuning -----------------------------------------------------------------------------
 struct Tuning {
   int32_t split_blocks = 0;       // 0 = automatic
-  int32_t target_waves = 16384;
+  int32_t target_waves = 0;       // 0: 8192 wave items (vector-ALU decode), 4096 (matrix-core decode)
   int32_t overlap_prefill = 0;    // 1 = run prefill tiles on a side stream beside decode rows
   int32_t xcds = 8;               // XCDs that work-groups are dispatched over (MI355X: 8)
   int32_t prefill_touch = 0;      // 1: prefill pulls key tiles two steps ahead toward L2
@@ -322,7 +322,10 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
   int32_t split = g_tuning.split_blocks;
   if (split <= 0) {
     const int64_t units = total_blocks * s->num_kv_heads * p.n_sub;
-    const int64_t target = std::max<int32_t>(g_tuning.target_waves, 1);
+    // Longer splits mean fewer partials to write and merge; the target keeps enough items
+    // to fill the machine a few times over (the matrix-core kernel runs 3 waves per SIMD,
+    // the vector-ALU one more). Measured on configs 2, 3 and the trace replay.
+    const int64_t target = g_tuning.target_waves > 0 ? g_tuning.target_waves : (p.mfma_decode ? 4096 : 8192);
     split = static_cast<int32_t>(std::clamp<int64_t>((units + target - 1) / target, 4, kMaxSplitBlocks));
   }
   split = std::min(split, kMaxSplitBlocks);
