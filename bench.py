@@ -131,6 +131,11 @@ def main(argv=None):
     ap.add_argument("--api", choices=["fused", "split"], default="fused",
                     help="fused: one cb_step_forward call per step (one metadata upload); split: Batch upload + "
                          "cb_kv_append + cb_ragged_attention")
+    ap.add_argument("--compare-policies", action="store_true",
+                    help="offline throughput of the first --requests requests of the config-5 trace under "
+                         "continuous batching, naive padded batching (batch 32 and 8) and request-at-a-time, "
+                         "all through the same kernels")
+    ap.add_argument("--requests", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
                          "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
@@ -149,6 +154,8 @@ def main(argv=None):
     from ragged_continuous_batching_amd.runner import DeviceRun
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.compare_policies:
+        return bench_policies(args)
     if args.config == 5:
         return bench_trace(args)
     if args.copy_calibration:
@@ -382,6 +389,102 @@ def bench_trace(args):
                      "traffic": None},
         "device_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
         "kernels": kernels,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_policies(args):
+    """The baselines the pages compare continuous batching with, on one request set: the
+    first N requests of the config-5 trace, all waiting at the start, each policy run until
+    every request has finished. Same kernels, same entry point, same cache; only the step
+    builder's policy differs (cb_sched_set_static). Throughput = generated tokens (sum of
+    out_len) / wall time; rows = packed rows the kernels processed."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from ragged_continuous_batching_amd import cb
+    from ragged_continuous_batching_amd.runner import DeviceRun
+
+    wl = W.config(5)
+    reqs = [r for k in range(wl.steps) for r in wl.arrivals[k]][: args.requests]
+    run = DeviceRun(wl, stale=None)
+    stream = torch.cuda.current_stream()
+    policies = [("continuous", 0), ("naive-batch-32", 32), ("naive-batch-8", 8), ("request-at-a-time", 1)]
+
+    def fresh(b):
+        s = cb.Scheduler(wl.token_budget, wl.block_size, wl.num_blocks, wl.max_num_seqs, wl.free_list)
+        if b:
+            s.set_static(b)
+        for r in reqs:
+            s.add(r.req_id, r.prompt_len, r.out_len)
+        return s
+
+    # size the buffers from a dry run of every policy (host only)
+    max_t, max_ws, dry = 1, 256, {}
+    for name, b in policies:
+        s, steps, rows = fresh(b), 0, 0
+        while True:
+            st = s.build_raw()
+            if st.num_reqs == 0 and s.stats()[:2] == (0, 0):
+                break
+            if st.num_reqs == 0 and st.num_evicted == 0:
+                raise RuntimeError("a step with no rows while requests are left")
+            if st.num_reqs:
+                max_t = max(max_t, st.num_tokens)
+                max_ws = max(max_ws, cb.cb_step_workspace_size(run.shape, st.num_reqs, st.num_tokens,
+                                                               st.max_blocks_per_req, st.cu_q_lens, st.ctx_lens))
+                steps += 1
+                rows += st.num_tokens
+            s.commit()
+        dry[name] = (steps, rows)
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    q = torch.randn(max_t, wl.num_q_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    k_new = torch.randn(max_t, wl.num_kv_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    v_new = torch.randn(max_t, wl.num_kv_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    ws = torch.empty(max_ws, dtype=torch.uint8, device="cuda")
+
+    def drive(s, limit=None):
+        n = 0
+        while limit is None or n < limit:
+            st = s.build_raw()
+            if st.num_reqs == 0 and s.stats()[:2] == (0, 0):
+                break
+            if st.num_reqs == 0 and st.num_evicted == 0:
+                raise RuntimeError("a step with no rows while requests are left")
+            if st.num_reqs:
+                launch_step(cb, run, st, q, k_new, v_new, o, ws, stream)
+            s.commit()
+            n += 1
+
+    drive(fresh(0), limit=200)                      # warm-up (clocks, code objects)
+    torch.cuda.synchronize()
+    gen = int(sum(r.out_len for r in reqs))
+    useful = int(sum(r.prompt_len + r.out_len - 1 for r in reqs))
+    out = {}
+    for name, b in policies:
+        s = fresh(b)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        drive(s)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        steps, rows = dry[name]
+        out[name] = {"generated_tokens_per_s": round(gen / wall, 1), "seconds": round(wall, 4), "steps": steps,
+                     "rows": rows, "useful_row_fraction": round(useful / rows, 4)}
+    base = out["continuous"]["generated_tokens_per_s"]
+    result = {
+        "metric": "generated tokens/s, offline, per scheduling policy",
+        "value": base, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"first {len(reqs)} requests of the scheduler trace (lognormal prompts, geometric "
+                               "outputs), all waiting at the start", "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "token_budget": wl.token_budget,
+                   "generated_tokens": gen, "useful_rows": useful},
+        "policies": out,
+        "continuous_over": {n: round(base / v["generated_tokens_per_s"], 2) for n, v in out.items() if n != "continuous"},
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -236,6 +236,21 @@ typedef struct {
  * allocation order, or NULL for 0,1,2,... Returns NULL on invalid arguments. */
 cb_sched* cb_sched_create(int32_t token_budget, int32_t block_size, int32_t num_blocks,
                           int32_t max_num_seqs, const int32_t* initial_free_list);
+/* Switches the builder to naive batching, the baseline the pages contrast continuous
+ * batching with (zhangchitc "continuous-batching", section "Naive batching: the whole batch
+ * finishes together"; hassanahmed "How continuous batching speeds up LLM serving", the batch
+ * loop that returns results when the batch finishes; batch_size 1 is request-at-a-time).
+ * From then on each build():
+ *   1. if every running request is done, evicts them all (blocks to the free list tail);
+ *   2. with nothing running, admits up to batch_size waiting requests (FIFO) while the free
+ *      list holds ceil(P / block_size) blocks for each of them, P being the longest prompt
+ *      among them, and emits one prefill step of P rows per request: the prompt, then
+ *      P - prompt_len pad rows (causal attention keeps pads out of the prompt's rows);
+ *      commit() then sets the context to prompt_len, so the first decode row overwrites the
+ *      first pad slot;
+ *   3. otherwise emits one decode row for every running request, done ones included.
+ * m does not apply. Call before any request runs (CB_ERR_STATE otherwise). */
+int cb_sched_set_static(cb_sched* s, int32_t batch_size);
 /* A new request enters the waiting queue. prompt_len >= 1, out_len >= 1. */
 int cb_sched_add(cb_sched* s, int64_t req_id, int32_t prompt_len, int32_t out_len);
 /* A request that is already running with `cached` positions in the cache: either still in

@@ -29,6 +29,17 @@ Readings where the pages are silent (both the C++ builder and this reference tak
 * ``out_len`` counts the token produced by the last prefill chunk. A request is done once
   it has produced ``out_len`` tokens, or when the caller flags EOS for a step in which it
   produced a token. Done requests are evicted at the start of the next build.
+
+``set_static(B)`` switches to the naive batching the pages contrast this with (zhangchitc
+"continuous-batching", section "Naive batching: the whole batch finishes together";
+hassanahmed, the batch loop that returns results when the batch finishes; B = 1 is
+request-at-a-time): up to B waiting requests start together, every prompt is padded to the
+longest one P and prefilled in one step, then every member decodes one row per step, done
+ones included, until all are done, and only then do they all leave. Readings: pads are rows
+after the prompt (positions prompt_len .. P-1, causally invisible to the prompt's rows) and
+hold no context afterwards (the first decode row overwrites position prompt_len); admission
+stops at the first request for which the free list cannot hold ceil(P / bs) blocks for every
+member so far; the token budget m does not apply.
 """
 from __future__ import annotations
 
@@ -88,6 +99,11 @@ class RefScheduler:
         self.waiting: deque[_Req] = deque()
         self.running: list[_Req] = []
         self.pending = None
+        self.static_b = 0
+
+    def set_static(self, batch_size: int) -> None:
+        assert batch_size >= 1 and not self.running and self.pending is None
+        self.static_b = int(batch_size)
 
     # ---- requests ----------------------------------------------------------------------
     def add(self, req_id: int, prompt_len: int, out_len: int) -> None:
@@ -109,6 +125,8 @@ class RefScheduler:
     # ---- one step ----------------------------------------------------------------------
     def build(self) -> Step:
         assert self.pending is None, "commit the previous step first"
+        if self.static_b:
+            return self._build_static()
         bs = self.bs
         evicted = []
         for r in self.running:                              # 1. evict finished
@@ -155,6 +173,43 @@ class RefScheduler:
             budget -= q
 
         batch = [(r, 1) for r in decodes] + chunks
+        return self._emit(batch, len(decodes), evicted, admitted)
+
+    def _build_static(self) -> Step:
+        bs = self.bs
+        evicted, admitted = [], []
+        if self.running and all(r.done for r in self.running):      # the batch finished
+            for r in self.running:
+                self.free.extend(r.blocks)
+                r.blocks = []
+                evicted.append(r.req_id)
+            self.running = []
+        if not self.running:                                          # next batch: padded prefill
+            members, P = [], 0
+            for w in list(self.waiting)[: self.static_b]:
+                P2 = max(P, w.prompt_len)
+                if (len(members) + 1) * _ceil(P2, bs) > len(self.free):
+                    break
+                members.append(w)
+                P = P2
+            if not members and self.waiting:
+                raise OutOfBlocks("padded prompt")
+            for w in members:
+                self.waiting.popleft()
+                w.blocks = [self.free.popleft() for _ in range(_ceil(P, bs))]
+                self.running.append(w)
+                admitted.append(w.req_id)
+            return self._emit([(w, P) for w in members], 0, evicted, admitted)
+        need = sum(max(0, _ceil(r.ctx + 1, bs) - len(r.blocks)) for r in self.running)
+        if need > len(self.free):
+            raise OutOfBlocks("decode")
+        for r in self.running:
+            while len(r.blocks) < _ceil(r.ctx + 1, bs):
+                r.blocks.append(self.free.popleft())
+        return self._emit([(r, 1) for r in self.running], len(self.running), evicted, admitted)
+
+    def _emit(self, batch, num_decode, evicted, admitted) -> Step:
+        bs = self.bs
         R = len(batch)
         cu = np.zeros(R + 1, dtype=np.int32)
         ctx = np.zeros(R, dtype=np.int32)
@@ -175,12 +230,13 @@ class RefScheduler:
                 owner[cu[i] + k] = i
         self.pending = batch
         return Step(np.array([r.req_id for r, _ in batch], dtype=np.int64), cu, ctx, bt, slots, owner,
-                    len(decodes), evicted, admitted)
+                    num_decode, evicted, admitted)
 
     def commit(self, eos=None) -> None:
         assert self.pending is not None, "no step to commit"
         for i, (r, q) in enumerate(self.pending):
-            r.ctx += q
+            # a padded prefill (naive batching) ends at the prompt: pad rows hold no context
+            r.ctx = min(r.ctx + q, r.prompt_len) if r.ctx < r.prompt_len else r.ctx + q
             if r.ctx >= r.prompt_len:                       # this step produced a token
                 r.gen += 1
                 if r.gen >= r.out_len or (eos is not None and bool(eos[i])):

@@ -85,6 +85,7 @@ def _load():
         "cb_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "cb_sched_create": (P, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
         "cb_sched_add": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+        "cb_sched_set_static": (ctypes.c_int, [P, ctypes.c_int32]),
         "cb_sched_add_cached": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32]),
         "cb_sched_build": (ctypes.c_int, [P, ctypes.POINTER(cb_step)]),
@@ -105,7 +106,7 @@ EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_att
             "cb_step_forward", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_reset",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
-            "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats")
+            "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static")
 
 
 def _check(status: int) -> int:
@@ -260,6 +261,10 @@ class Scheduler:
 
     def add(self, req_id: int, prompt_len: int, out_len: int) -> None:
         _check(lib.cb_sched_add(self._h, int(req_id), int(prompt_len), int(out_len)))
+
+    def set_static(self, batch_size: int) -> None:
+        """Naive padded batching of up to batch_size requests (1 = request-at-a-time)."""
+        _check(lib.cb_sched_set_static(self._h, int(batch_size)))
 
     def add_cached(self, req_id: int, prompt_len: int, out_len: int, cached: int, generated: int) -> None:
         _check(lib.cb_sched_add_cached(self._h, int(req_id), int(prompt_len), int(out_len), int(cached),

@@ -36,6 +36,7 @@ inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a +
 
 struct cb_sched {
   int32_t m, bs, max_num_seqs, num_blocks;
+  int32_t static_b = 0;                // > 0: naive padded batches of up to this many requests
   std::deque<int32_t> free_list;
   std::deque<Req> waiting;
   std::vector<Req> running;            // admission order
@@ -88,6 +89,14 @@ extern "C" cb_sched* cb_sched_clone(const cb_sched* s) {
   return c;
 }
 
+extern "C" int cb_sched_set_static(cb_sched* s, int32_t batch_size) {
+  if (!s || batch_size < 1) return cb::fail(CB_ERR_INVALID_ARG, "cb_sched_set_static: batch_size must be >= 1");
+  if (s->has_pending || !s->running.empty())
+    return cb::fail(CB_ERR_STATE, "cb_sched_set_static: requests are already running");
+  s->static_b = batch_size;
+  return CB_OK;
+}
+
 extern "C" int cb_sched_add(cb_sched* s, int64_t req_id, int32_t prompt_len, int32_t out_len) {
   if (!s || prompt_len < 1 || out_len < 1)
     return cb::fail(CB_ERR_INVALID_ARG, "cb_sched_add: prompt_len and out_len must be >= 1");
@@ -126,83 +135,154 @@ extern "C" int cb_sched_add_cached(cb_sched* s, int64_t req_id, int32_t prompt_l
   return CB_OK;
 }
 
+namespace {
+
+// Naive batching (hassanahmed "How continuous batching speeds up LLM serving", the batch
+// loop that returns results when the batch finishes; zhangchitc "continuous-batching",
+// section "Naive batching: the whole batch finishes together"; Hugging Face blog, section
+// "Continuous batching", batched generation with padding): up to B waiting requests start
+// together, every prompt is padded to the longest one and prefilled in one step, then every
+// member decodes one row per step, finished ones included, until all are done; only then do
+// they leave and the next batch starts. Pad rows sit after the prompt, at positions
+// prompt_len .. P-1, where causal attention keeps them out of the prompt's rows; the first
+// decode row overwrites position prompt_len. The token budget m does not apply.
+int build_static(cb_sched* s, std::vector<std::pair<int32_t, int32_t>>& batch, int32_t& num_decode) {
+  const int32_t bs = s->bs;
+  bool all_done = !s->running.empty();
+  for (const auto& r : s->running) all_done = all_done && r.done;
+  if (all_done) {                      // the batch has finished: everyone leaves together
+    for (auto& r : s->running) {
+      for (int32_t b : r.blocks) s->free_list.push_back(b);
+      s->evicted.push_back(r.id);
+    }
+    s->running.clear();
+  }
+  if (s->running.empty()) {            // start the next batch with its padded prefill
+    int32_t k = 0, P = 0;
+    while (k < s->static_b && k < static_cast<int32_t>(s->waiting.size())) {
+      const int32_t P2 = std::max(P, s->waiting[k].prompt_len);
+      if (static_cast<int64_t>(k + 1) * ceil_div(P2, bs) > static_cast<int64_t>(s->free_list.size())) break;
+      P = P2;
+      ++k;
+    }
+    if (k == 0 && !s->waiting.empty())
+      return cb::fail(CB_ERR_OUT_OF_BLOCKS, "cb_sched_build: free list cannot hold the padded prompt");
+    for (int32_t i = 0; i < k; ++i) {
+      Req r = std::move(s->waiting.front());
+      s->waiting.pop_front();
+      for (int32_t j = 0; j < ceil_div(P, bs); ++j) {
+        r.blocks.push_back(s->free_list.front());
+        s->free_list.pop_front();
+      }
+      s->admitted.push_back(r.id);
+      s->running.push_back(std::move(r));
+      batch.emplace_back(i, P);
+    }
+    num_decode = 0;
+    return CB_OK;
+  }
+  int64_t need = 0;                    // one decode row for every member
+  for (const auto& r : s->running)
+    need += std::max<int64_t>(0, ceil_div(r.ctx + 1, bs) - static_cast<int64_t>(r.blocks.size()));
+  if (need > static_cast<int64_t>(s->free_list.size()))
+    return cb::fail(CB_ERR_OUT_OF_BLOCKS, "cb_sched_build: free list cannot hold the decode tokens");
+  for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()); ++i) {
+    Req& r = s->running[i];
+    while (static_cast<int32_t>(r.blocks.size()) < ceil_div(r.ctx + 1, bs)) {
+      r.blocks.push_back(s->free_list.front());
+      s->free_list.pop_front();
+    }
+    batch.emplace_back(i, 1);
+  }
+  num_decode = static_cast<int32_t>(batch.size());
+  return CB_OK;
+}
+
+}  // namespace
+
 extern "C" int cb_sched_build(cb_sched* s, cb_step* out) {
   if (!s || !out) return cb::fail(CB_ERR_INVALID_ARG, "cb_sched_build: null argument");
   if (s->has_pending) return cb::fail(CB_ERR_STATE, "cb_sched_build: commit the previous step first");
   const int32_t bs = s->bs;
   s->evicted.clear();
   s->admitted.clear();
+  std::vector<std::pair<int32_t, int32_t>> batch;
+  int32_t num_decode = 0;
+  if (s->static_b > 0) {
+    const int st = build_static(s, batch, num_decode);
+    if (st != CB_OK) return st;
+  } else {
 
-  // 1. evict finished requests; their blocks go to the tail of the free list in table order
-  {
-    std::vector<Req> keep;
-    keep.reserve(s->running.size());
-    for (auto& r : s->running) {
-      if (r.done) {
-        for (int32_t b : r.blocks) s->free_list.push_back(b);
-        s->evicted.push_back(r.id);
-      } else {
-        keep.push_back(std::move(r));
+    // 1. evict finished requests; their blocks go to the tail of the free list in table order
+    {
+      std::vector<Req> keep;
+      keep.reserve(s->running.size());
+      for (auto& r : s->running) {
+        if (r.done) {
+          for (int32_t b : r.blocks) s->free_list.push_back(b);
+          s->evicted.push_back(r.id);
+        } else {
+          keep.push_back(std::move(r));
+        }
+      }
+      s->running.swap(keep);
+    }
+
+    // 2. decode-phase requests first, one token each (at most m)
+    int64_t need = 0;
+    for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()); ++i) {
+      const Req& r = s->running[i];
+      if (r.ctx >= r.prompt_len) {
+        if (static_cast<int32_t>(batch.size()) == s->m) break;
+        batch.emplace_back(i, 1);
+        need += std::max<int64_t>(0, ceil_div(r.ctx + 1, bs) - static_cast<int64_t>(r.blocks.size()));
       }
     }
-    s->running.swap(keep);
-  }
+    if (need > static_cast<int64_t>(s->free_list.size()))
+      return cb::fail(CB_ERR_OUT_OF_BLOCKS, "cb_sched_build: free list cannot hold the decode tokens");
+    for (auto& [i, q] : batch) {
+      Req& r = s->running[i];
+      while (static_cast<int32_t>(r.blocks.size()) < ceil_div(r.ctx + 1, bs)) {
+        r.blocks.push_back(s->free_list.front());
+        s->free_list.pop_front();
+      }
+    }
+    num_decode = static_cast<int32_t>(batch.size());
+    int64_t budget = s->m - num_decode;
 
-  // 2. decode-phase requests first, one token each (at most m)
-  std::vector<std::pair<int32_t, int32_t>> batch;
-  int64_t need = 0;
-  for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()); ++i) {
-    const Req& r = s->running[i];
-    if (r.ctx >= r.prompt_len) {
-      if (static_cast<int32_t>(batch.size()) == s->m) break;
-      batch.emplace_back(i, 1);
-      need += std::max<int64_t>(0, ceil_div(r.ctx + 1, bs) - static_cast<int64_t>(r.blocks.size()));
+    // 3. continue partly prefilled requests
+    for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()) && budget > 0; ++i) {
+      Req& r = s->running[i];
+      if (r.ctx >= r.prompt_len) continue;
+      int64_t cap = (static_cast<int64_t>(r.blocks.size()) + static_cast<int64_t>(s->free_list.size())) * bs - r.ctx;
+      int64_t q = std::min<int64_t>({static_cast<int64_t>(r.prompt_len - r.ctx), budget, cap});
+      if (q <= 0) continue;
+      while (static_cast<int64_t>(r.blocks.size()) < ceil_div(r.ctx + q, bs)) {
+        r.blocks.push_back(s->free_list.front());
+        s->free_list.pop_front();
+      }
+      batch.emplace_back(i, static_cast<int32_t>(q));
+      budget -= q;
     }
-  }
-  if (need > static_cast<int64_t>(s->free_list.size()))
-    return cb::fail(CB_ERR_OUT_OF_BLOCKS, "cb_sched_build: free list cannot hold the decode tokens");
-  for (auto& [i, q] : batch) {
-    Req& r = s->running[i];
-    while (static_cast<int32_t>(r.blocks.size()) < ceil_div(r.ctx + 1, bs)) {
-      r.blocks.push_back(s->free_list.front());
-      s->free_list.pop_front();
-    }
-  }
-  const int32_t num_decode = static_cast<int32_t>(batch.size());
-  int64_t budget = s->m - num_decode;
 
-  // 3. continue partly prefilled requests
-  for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()) && budget > 0; ++i) {
-    Req& r = s->running[i];
-    if (r.ctx >= r.prompt_len) continue;
-    int64_t cap = (static_cast<int64_t>(r.blocks.size()) + static_cast<int64_t>(s->free_list.size())) * bs - r.ctx;
-    int64_t q = std::min<int64_t>({static_cast<int64_t>(r.prompt_len - r.ctx), budget, cap});
-    if (q <= 0) continue;
-    while (static_cast<int64_t>(r.blocks.size()) < ceil_div(r.ctx + q, bs)) {
-      r.blocks.push_back(s->free_list.front());
-      s->free_list.pop_front();
+    // 4. admit waiting requests while can_admit holds (FIFO; the first misfit stops admission)
+    while (!s->waiting.empty() && budget > 0 &&
+           (s->max_num_seqs == 0 || static_cast<int32_t>(s->running.size()) < s->max_num_seqs)) {
+      Req& w = s->waiting.front();
+      int64_t q = std::min<int64_t>(w.prompt_len, budget);
+      int32_t nb = ceil_div(q, bs);
+      if (nb > static_cast<int32_t>(s->free_list.size())) break;
+      Req r = std::move(w);
+      s->waiting.pop_front();
+      for (int32_t k = 0; k < nb; ++k) {
+        r.blocks.push_back(s->free_list.front());
+        s->free_list.pop_front();
+      }
+      s->admitted.push_back(r.id);
+      s->running.push_back(std::move(r));
+      batch.emplace_back(static_cast<int32_t>(s->running.size()) - 1, static_cast<int32_t>(q));
+      budget -= q;
     }
-    batch.emplace_back(i, static_cast<int32_t>(q));
-    budget -= q;
-  }
-
-  // 4. admit waiting requests while can_admit holds (FIFO; the first misfit stops admission)
-  while (!s->waiting.empty() && budget > 0 &&
-         (s->max_num_seqs == 0 || static_cast<int32_t>(s->running.size()) < s->max_num_seqs)) {
-    Req& w = s->waiting.front();
-    int64_t q = std::min<int64_t>(w.prompt_len, budget);
-    int32_t nb = ceil_div(q, bs);
-    if (nb > static_cast<int32_t>(s->free_list.size())) break;
-    Req r = std::move(w);
-    s->waiting.pop_front();
-    for (int32_t k = 0; k < nb; ++k) {
-      r.blocks.push_back(s->free_list.front());
-      s->free_list.pop_front();
-    }
-    s->admitted.push_back(r.id);
-    s->running.push_back(std::move(r));
-    batch.emplace_back(static_cast<int32_t>(s->running.size()) - 1, static_cast<int32_t>(q));
-    budget -= q;
   }
 
   // 5. emit the packed step
@@ -258,7 +338,8 @@ extern "C" int cb_sched_commit(cb_sched* s, const uint8_t* eos) {
   if (!s->has_pending) return cb::fail(CB_ERR_STATE, "cb_sched_commit: no step to commit");
   for (size_t k = 0; k < s->pending.size(); ++k) {
     Req& r = s->running[s->pending[k].first];
-    r.ctx += s->pending[k].second;
+    // a padded prefill row set (naive batching) ends at the prompt: pads hold no context
+    r.ctx = r.ctx < r.prompt_len ? std::min(r.ctx + s->pending[k].second, r.prompt_len) : r.ctx + s->pending[k].second;
     if (r.ctx >= r.prompt_len) {      // this step produced an output token
       r.gen += 1;
       if (r.gen >= r.out_len || (eos && eos[k])) r.done = true;

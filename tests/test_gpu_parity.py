@@ -338,3 +338,29 @@ def test_config5_trace_replay():
             checked += 1
         run.sched.commit()
     assert checked == 11
+
+
+@pytest.mark.parametrize("batch_size", [1, 3])
+def test_static_batching_steps(batch_size):
+    """Naive padded batching runs through the same kernels: every row of every step,
+    pad rows and the rows of finished members included, matches the oracle (cache values
+    depend only on (request, position), so a pad slot that a decode row later overwrites
+    holds the same value either way)."""
+    reqs = [W.Request(0, 37, 3), W.Request(1, 5, 6), W.Request(2, 130, 2), W.Request(3, 1, 4), W.Request(4, 64, 1)]
+    wl = W.custom(reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", seed=9)
+    run = DeviceRun(wl)
+    run.sched.set_static(batch_size)
+    n = 0
+    while True:
+        step = run.sched.build()
+        if step.num_reqs == 0:
+            break
+        _, batch, q, k, v, o = run.run_step(step)
+        torch.cuda.synchronize()
+        check(o, oracle_full(wl, step), "bf16", f"static B={batch_size} step {n} (T={step.num_tokens})")
+        run.sched.commit()
+        n += 1
+    expect = 0
+    for i in range(0, len(reqs), batch_size):
+        expect += max(r.out_len for r in reqs[i:i + batch_size])
+    assert n == expect

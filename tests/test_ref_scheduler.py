@@ -192,3 +192,101 @@ def test_trace_invariants_small():
 def test_trace_invariants_config5_head():
     wl = W.config(5)
     check_trace_invariants(wl, 60)
+
+
+# ---- naive batching (the baseline the pages contrast continuous batching with) ----------
+def run_to_completion(s, eos_at=None, max_steps=100000):
+    """Builds and commits until idle; returns the non-empty steps (the last build only
+    evicts the final batch and runs no rows)."""
+    steps = []
+    while not s.idle() and len(steps) < max_steps:
+        st = s.build()
+        eos = None
+        if eos_at is not None:
+            eos = np.array([eos_at(len(steps), int(rid)) for rid in st.req_ids], dtype=np.uint8)
+        s.commit(eos)
+        if st.num_reqs:
+            steps.append(st)
+    return steps
+
+
+def test_static_batch_pads_to_longest_and_finishes_together():
+    """zhangchitc "continuous-batching", "Naive batching": A, B and C arrive together, are
+    padded to the longest and keep computing until every one of them has finished."""
+    s = RefScheduler(token_budget=4, block_size=4, num_blocks=64)
+    s.set_static(3)
+    for rid, (p, o) in enumerate([(5, 2), (2, 4), (3, 3)]):
+        s.add(rid, p, o)
+    s.add(3, 2, 1)                                   # waits for the next batch
+    steps = run_to_completion(s)
+    first = steps[0]
+    assert first.req_ids.tolist() == [0, 1, 2] and np.diff(first.cu_q_lens).tolist() == [5, 5, 5]
+    assert first.num_tokens == 15 > 4                 # the token budget does not apply
+    assert first.ctx_lens.tolist() == [0, 0, 0] and first.num_decode == 0
+    # longest output is 4: three decode steps with all three members, done ones included
+    for k, ctx in zip((1, 2, 3), ([5, 2, 3], [6, 3, 4], [7, 4, 5])):
+        assert steps[k].req_ids.tolist() == [0, 1, 2] and steps[k].ctx_lens.tolist() == ctx
+        assert steps[k].num_decode == 3 and steps[k].num_tokens == 3
+    assert steps[4].evicted == [0, 1, 2] and steps[4].req_ids.tolist() == [3]
+    assert len(steps) == 5                            # request 3: prefill only (out_len 1)
+
+
+def test_static_request_at_a_time():
+    """Batch size 1: no pads; each request takes 1 + (out_len - 1) steps on its own."""
+    reqs = [(7, 3), (1, 5), (12, 1), (4, 2)]
+    s = RefScheduler(token_budget=2, block_size=4, num_blocks=32)
+    s.set_static(1)
+    for rid, (p, o) in enumerate(reqs):
+        s.add(rid, p, o)
+    steps = run_to_completion(s)
+    assert len(steps) == sum(o for _, o in reqs)
+    assert all(st.num_reqs == 1 for st in steps)
+    rows = {}
+    for st in steps:
+        rows[int(st.req_ids[0])] = rows.get(int(st.req_ids[0]), 0) + st.num_tokens
+    assert rows == {rid: p + o - 1 for rid, (p, o) in enumerate(reqs)}
+
+
+def test_static_eos_ends_the_batch_early():
+    s = RefScheduler(token_budget=8, block_size=4, num_blocks=64)
+    s.set_static(2)
+    s.add(0, 3, 50)
+    s.add(1, 4, 50)
+    s.add(2, 2, 1)
+    steps = run_to_completion(s, eos_at=lambda k, rid: k == 2)   # both flag EOS at step 2
+    assert [st.req_ids.tolist() for st in steps] == [[0, 1], [0, 1], [0, 1], [2]]
+    assert steps[3].evicted == [0, 1]
+
+
+def test_static_closed_form_on_a_trace():
+    """Rows processed = sum over batches of size x (P + O - 1), with P the longest prompt and
+    O the longest output of the batch; rows useful = sum of prompt + out - 1; every block is
+    accounted for at every step."""
+    wl = W.trace_workload(seed=5, steps=40, rate=1.2, prompt_median=30, prompt_max=200, out_mean=15,
+                          token_budget=64, num_blocks=4000)
+    reqs = [r for k in range(wl.steps) for r in wl.arrivals[k]][:40]
+    for B in (1, 3, 8):
+        s = RefScheduler(wl.token_budget, wl.block_size, wl.num_blocks)
+        s.set_static(B)
+        for r in reqs:
+            s.add(r.req_id, r.prompt_len, r.out_len)
+        steps = run_to_completion(s)
+        expect_rows, expect_steps = 0, 0
+        for i in range(0, len(reqs), B):
+            grp = reqs[i:i + B]
+            P, O = max(r.prompt_len for r in grp), max(r.out_len for r in grp)
+            expect_rows += len(grp) * (P + O - 1)
+            expect_steps += O
+        assert sum(st.num_tokens for st in steps) == expect_rows
+        assert len(steps) == expect_steps
+        assert s.num_free_blocks == wl.num_blocks
+        useful = sum(r.prompt_len + r.out_len - 1 for r in reqs)
+        assert expect_rows >= useful and (B > 1 or expect_rows == useful)
+
+
+def test_static_padded_prompt_out_of_blocks():
+    s = RefScheduler(token_budget=8, block_size=4, num_blocks=3)
+    s.set_static(2)
+    s.add(0, 20, 2)
+    with pytest.raises(OutOfBlocks):
+        s.build()

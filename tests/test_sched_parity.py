@@ -105,3 +105,39 @@ def test_clone_replays_the_same_step():
     nxt = c1.build()                                   # the clone advances on its own
     assert np.array_equal(nxt.ctx_lens[:64], a.ctx_lens[:64] + 1)
     same_step(lib.build(), b)                          # the original is untouched
+
+
+@pytest.mark.parametrize("batch_size,eos_rate", [(1, 0.0), (4, 0.0), (16, 0.05), (64, 0.0)])
+def test_static_batching_matches_reference(batch_size, eos_rate):
+    """Naive padded batching (cb_sched_set_static) step by step against the reference, on a
+    trace with arrivals interleaved with the steps, until everything has finished."""
+    wl = W.trace_workload(seed=31, steps=120, rate=1.0, prompt_median=40, prompt_max=300, out_mean=25,
+                          token_budget=64, num_blocks=20000)
+    ref, lib = pair(wl)
+    ref.set_static(batch_size)
+    lib.set_static(batch_size)
+    rng = np.random.default_rng(batch_size)
+    k = 0
+    while k < wl.steps or not ref.idle():
+        if k < wl.steps:
+            for r in wl.arrivals[k]:
+                ref.add(r.req_id, r.prompt_len, r.out_len)
+                lib.add(r.req_id, r.prompt_len, r.out_len)
+        a, b = ref.build(), lib.build()
+        same_step(a, b)
+        eos = (rng.random(a.num_reqs) < eos_rate).astype(np.uint8) if eos_rate else None
+        ref.commit(eos)
+        lib.commit(eos)
+        assert lib.stats() == (len(ref.running), len(ref.waiting), ref.num_free_blocks)
+        k += 1
+        assert k < 20000
+    assert ref.num_free_blocks == wl.num_blocks
+
+
+def test_static_batching_set_after_start_is_rejected():
+    lib = cb.Scheduler(64, 16, 100)
+    lib.add(0, 10, 2)
+    lib.build()
+    lib.commit()
+    with pytest.raises(cb.CbError):
+        lib.set_static(4)
