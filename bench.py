@@ -136,6 +136,10 @@ def main(argv=None):
                          "continuous batching, naive padded batching (batch 32 and 8) and request-at-a-time, "
                          "all through the same kernels")
     ap.add_argument("--requests", type=int, default=256)
+    ap.add_argument("--pool-blocks", type=int, default=0,
+                    help="config 5 only: a KV pool of this many blocks with preemption by recompute "
+                         "(0 = the configured pool, which never fills)")
+    ap.add_argument("--watermark", type=int, default=0, help="blocks kept free at admission with --pool-blocks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
                          "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
@@ -295,7 +299,11 @@ def bench_trace(args):
     total_steps = wl.steps
     warm = min(args.warmup, total_steps - 1)
     steps = min(args.steps if args.steps != 50 else total_steps - warm, total_steps - warm)
-    run = DeviceRun(wl, stale=None)
+    sched = None
+    if args.pool_blocks:
+        sched = cb.Scheduler(wl.token_budget, wl.block_size, args.pool_blocks, wl.max_num_seqs)
+        sched.set_preemption(True, args.watermark)
+    run = DeviceRun(wl, stale=None, sched=sched)
     g = torch.Generator(device="cuda").manual_seed(wl.seed)
     m = wl.token_budget
     q = torch.randn(m, wl.num_q_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
@@ -304,11 +312,12 @@ def bench_trace(args):
     o = torch.empty_like(q)
     # dry run of the schedule on a copy: the largest workspace any step needs
     dry = run.sched.clone()
-    need, alg_dec_bytes, tokens = 0, [], []
+    need, alg_dec_bytes, tokens, preempted = 0, [], [], []
     for kstep in range(total_steps):
         for r in wl.arrivals[kstep]:
             dry.add(r.req_id, r.prompt_len, r.out_len)
         st = dry.build()
+        preempted.append(len(st.preempted))
         b = cb.cb_batch(st.num_reqs, st.num_tokens, st.max_blocks_per_req, 256, 256, 256,
                         st.cu_q_lens.ctypes.data, st.ctx_lens.ctypes.data)
         need = max(need, cb.cb_ragged_attention_workspace_size(run.shape, b),
@@ -382,8 +391,11 @@ def bench_trace(args):
         "data": "synthetic",
         "config": {"workload": "scheduler-trace replay (500 steps, Poisson(8) arrivals, lognormal prompts, "
                                "geometric outputs)", "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
-                   "head_dim": wl.head_dim, "token_budget": m, "num_blocks": wl.num_blocks, "seed": wl.seed,
-                   "tokens_timed": T_total, "api": args.api},
+                   "head_dim": wl.head_dim, "token_budget": m,
+                   "num_blocks": args.pool_blocks or wl.num_blocks, "seed": wl.seed,
+                   "tokens_timed": T_total, "api": args.api,
+                   "preemptions_timed": int(sum(preempted[warm:warm + steps])),
+                   "watermark": args.watermark if args.pool_blocks else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
                      "traffic": None},

@@ -230,6 +230,8 @@ typedef struct {
   int32_t num_admitted;
   const int64_t* evicted;         /* request ids evicted at the start of this build */
   const int64_t* admitted;        /* request ids admitted by this build */
+  int32_t num_preempted;
+  const int64_t* preempted;       /* request ids preempted by this build (back to waiting) */
 } cb_step;
 
 /* initial_free_list: host int32 [num_blocks], a permutation of 0..num_blocks-1 giving the
@@ -251,6 +253,15 @@ cb_sched* cb_sched_create(int32_t token_budget, int32_t block_size, int32_t num_
  *   3. otherwise emits one decode row for every running request, done ones included.
  * m does not apply. Call before any request runs (CB_ERR_STATE otherwise). */
 int cb_sched_set_static(cb_sched* s, int32_t batch_size);
+/* Preemption by recompute (hassanahmed "How continuous batching speeds up LLM serving",
+ * paged-memory section: when the card fills, a request is evicted for a while and brought
+ * back later). enable = 1: when the decode tokens of a build need more blocks than the free
+ * list holds, the most recently admitted running request gives back all its blocks and goes
+ * to the head of the waiting queue, repeatedly, until they fit. Re-admitted, it prefills all
+ * prompt_len + generated tokens it has (chunked like any prompt); the last of them yields its
+ * next token. watermark_blocks: admission also requires that many blocks to stay free (0 =
+ * admit while the first chunk fits). Not with naive batching (CB_ERR_STATE). */
+int cb_sched_set_preemption(cb_sched* s, int32_t enable, int32_t watermark_blocks);
 /* A new request enters the waiting queue. prompt_len >= 1, out_len >= 1. */
 int cb_sched_add(cb_sched* s, int64_t req_id, int32_t prompt_len, int32_t out_len);
 /* A request that is already running with `cached` positions in the cache: either still in

@@ -26,6 +26,12 @@ Readings where the pages are silent (both the C++ builder and this reference tak
 * Blocks are allocated lazily so request r holds ceil((c_r + q_r) / bs) blocks after the
   step is built. They come from the head of a FIFO free list. On eviction they go back to
   the tail, in block-table order.
+* Preemption (``set_preemption``; hassanahmed, paged-memory section: when the card fills, a
+  request is evicted for a while and brought back later), read as recompute: while the decode
+  tokens need more blocks than are free, the most recently admitted running request returns
+  all its blocks and goes to the head of the waiting queue; re-admitted, it prefills its
+  prompt and the tokens it generated (chunked like any prompt), and the last of them yields
+  its next token. A watermark keeps that many blocks free at admission.
 * ``out_len`` counts the token produced by the last prefill chunk. A request is done once
   it has produced ``out_len`` tokens, or when the caller flags EOS for a step in which it
   produced a token. Done requests are evicted at the start of the next build.
@@ -58,6 +64,7 @@ class _Req:
     req_id: int
     prompt_len: int
     out_len: int
+    pre_len: int = 0          # positions to prefill before decoding (set on creation)
     ctx: int = 0
     gen: int = 0
     blocks: list = field(default_factory=list)
@@ -75,6 +82,7 @@ class Step:
     num_decode: int
     evicted: list
     admitted: list
+    preempted: list = field(default_factory=list)
 
     @property
     def num_reqs(self) -> int:
@@ -100,19 +108,24 @@ class RefScheduler:
         self.running: list[_Req] = []
         self.pending = None
         self.static_b = 0
+        self.preempt, self.watermark = False, 0
+
+    def set_preemption(self, enable: bool, watermark_blocks: int = 0) -> None:
+        assert watermark_blocks >= 0 and not (enable and self.static_b)
+        self.preempt, self.watermark = bool(enable), int(watermark_blocks)
 
     def set_static(self, batch_size: int) -> None:
-        assert batch_size >= 1 and not self.running and self.pending is None
+        assert batch_size >= 1 and not self.running and self.pending is None and not self.preempt
         self.static_b = int(batch_size)
 
     # ---- requests ----------------------------------------------------------------------
     def add(self, req_id: int, prompt_len: int, out_len: int) -> None:
         assert prompt_len >= 1 and out_len >= 1
-        self.waiting.append(_Req(int(req_id), int(prompt_len), int(out_len)))
+        self.waiting.append(_Req(int(req_id), int(prompt_len), int(out_len), int(prompt_len)))
 
     def add_cached(self, req_id: int, prompt_len: int, out_len: int, cached: int, generated: int) -> None:
         """A running request whose first ``cached`` positions are already in the cache."""
-        r = _Req(int(req_id), int(prompt_len), int(out_len), int(cached), int(generated))
+        r = _Req(int(req_id), int(prompt_len), int(out_len), int(prompt_len), int(cached), int(generated))
         prefill_ok = r.gen == 0 and 0 <= r.ctx < r.prompt_len
         decode_ok = 1 <= r.gen < r.out_len and r.ctx == r.prompt_len + r.gen - 1
         assert prefill_ok or decode_ok, "inconsistent cached state"
@@ -136,8 +149,23 @@ class RefScheduler:
                 evicted.append(r.req_id)
         self.running = [r for r in self.running if not r.done]
 
-        decodes = [r for r in self.running if r.ctx >= r.prompt_len][: self.m]   # 2. decode first
-        need = sum(max(0, _ceil(r.ctx + 1, bs) - len(r.blocks)) for r in decodes)
+        def decode_rows():                                   # 2. decode first
+            dec = [r for r in self.running if r.ctx >= r.pre_len][: self.m]
+            return dec, sum(max(0, _ceil(r.ctx + 1, bs) - len(r.blocks)) for r in dec)
+        decodes, need = decode_rows()
+        preempted = []
+        # preemption: the most recently admitted request returns its blocks and goes back to
+        # the head of the queue; re-admitted, it prefills all tokens it has, the last of which
+        # yields its next token
+        while need > len(self.free) and self.preempt and self.running:
+            v = self.running.pop()
+            self.free.extend(v.blocks)
+            v.blocks = []
+            v.pre_len = v.prompt_len + v.gen
+            v.ctx = 0
+            preempted.append(v.req_id)
+            self.waiting.appendleft(v)
+            decodes, need = decode_rows()
         if need > len(self.free):
             raise OutOfBlocks("decode")
         for r in decodes:
@@ -149,9 +177,9 @@ class RefScheduler:
         for r in self.running:                              # 3. continue partial prefills
             if budget == 0:
                 break
-            if r.ctx >= r.prompt_len:
+            if r.ctx >= r.pre_len:
                 continue
-            q = min(r.prompt_len - r.ctx, budget, (len(r.blocks) + len(self.free)) * bs - r.ctx)
+            q = min(r.pre_len - r.ctx, budget, (len(r.blocks) + len(self.free)) * bs - r.ctx)
             if q <= 0:
                 continue
             while len(r.blocks) < _ceil(r.ctx + q, bs):
@@ -162,8 +190,8 @@ class RefScheduler:
         admitted = []
         while self.waiting and budget > 0 and (self.max_num_seqs == 0 or len(self.running) < self.max_num_seqs):
             w = self.waiting[0]                             # 4. admit while can_admit
-            q = min(w.prompt_len, budget)
-            if _ceil(q, bs) > len(self.free):
+            q = min(w.pre_len, budget)
+            if _ceil(q, bs) + self.watermark > len(self.free):
                 break
             self.waiting.popleft()
             w.blocks = [self.free.popleft() for _ in range(_ceil(q, bs))]
@@ -173,7 +201,9 @@ class RefScheduler:
             budget -= q
 
         batch = [(r, 1) for r in decodes] + chunks
-        return self._emit(batch, len(decodes), evicted, admitted)
+        step = self._emit(batch, len(decodes), evicted, admitted)
+        step.preempted = preempted
+        return step
 
     def _build_static(self) -> Step:
         bs = self.bs
@@ -236,8 +266,8 @@ class RefScheduler:
         assert self.pending is not None, "no step to commit"
         for i, (r, q) in enumerate(self.pending):
             # a padded prefill (naive batching) ends at the prompt: pad rows hold no context
-            r.ctx = min(r.ctx + q, r.prompt_len) if r.ctx < r.prompt_len else r.ctx + q
-            if r.ctx >= r.prompt_len:                       # this step produced a token
+            r.ctx = min(r.ctx + q, r.pre_len) if r.ctx < r.pre_len else r.ctx + q
+            if r.ctx >= r.pre_len:                          # this step produced a token
                 r.gen += 1
                 if r.gen >= r.out_len or (eos is not None and bool(eos[i])):
                     r.done = True

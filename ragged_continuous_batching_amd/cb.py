@@ -52,7 +52,7 @@ class cb_step(ctypes.Structure):
                 ("num_decode", ctypes.c_int32), ("req_ids", _i64p), ("cu_q_lens", _i32p), ("ctx_lens", _i32p),
                 ("block_tables", _i32p), ("slot_mapping", _i32p), ("token_to_req", _i32p),
                 ("num_evicted", ctypes.c_int32), ("num_admitted", ctypes.c_int32), ("evicted", _i64p),
-                ("admitted", _i64p)]
+                ("admitted", _i64p), ("num_preempted", ctypes.c_int32), ("preempted", _i64p)]
 
 
 def _load():
@@ -86,6 +86,7 @@ def _load():
         "cb_sched_create": (P, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
         "cb_sched_add": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
         "cb_sched_set_static": (ctypes.c_int, [P, ctypes.c_int32]),
+        "cb_sched_set_preemption": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32]),
         "cb_sched_add_cached": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_int32]),
         "cb_sched_build": (ctypes.c_int, [P, ctypes.POINTER(cb_step)]),
@@ -106,7 +107,8 @@ EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_att
             "cb_step_forward", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_reset",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
-            "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static")
+            "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
+            "cb_sched_set_preemption")
 
 
 def _check(status: int) -> int:
@@ -233,6 +235,7 @@ class Step:
         self.token_to_req = _arr(st.token_to_req, T, np.int32)
         self.evicted = _arr(st.evicted, st.num_evicted, np.int64).tolist()
         self.admitted = _arr(st.admitted, st.num_admitted, np.int64).tolist()
+        self.preempted = _arr(st.preempted, st.num_preempted, np.int64).tolist()
 
 
 class Scheduler:
@@ -261,6 +264,10 @@ class Scheduler:
 
     def add(self, req_id: int, prompt_len: int, out_len: int) -> None:
         _check(lib.cb_sched_add(self._h, int(req_id), int(prompt_len), int(out_len)))
+
+    def set_preemption(self, enable: bool, watermark_blocks: int = 0) -> None:
+        """Preemption by recompute when decode tokens do not fit the free list."""
+        _check(lib.cb_sched_set_preemption(self._h, 1 if enable else 0, int(watermark_blocks)))
 
     def set_static(self, batch_size: int) -> None:
         """Naive padded batching of up to batch_size requests (1 = request-at-a-time)."""

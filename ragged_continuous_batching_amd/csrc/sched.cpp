@@ -25,6 +25,8 @@ namespace {
 struct Req {
   int64_t id;
   int32_t prompt_len, out_len;
+  int32_t pre_len = 0;                 // positions to prefill before decoding (prompt, or all
+                                       // known tokens after a preemption)
   int32_t ctx = 0, gen = 0;
   std::vector<int32_t> blocks;
   bool done = false;
@@ -37,6 +39,7 @@ inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a +
 struct cb_sched {
   int32_t m, bs, max_num_seqs, num_blocks;
   int32_t static_b = 0;                // > 0: naive padded batches of up to this many requests
+  int32_t preempt = 0, watermark = 0;  // preemption by recompute; blocks kept free at admission
   std::deque<int32_t> free_list;
   std::deque<Req> waiting;
   std::vector<Req> running;            // admission order
@@ -44,7 +47,7 @@ struct cb_sched {
   std::vector<std::pair<int32_t, int32_t>> pending;
   bool has_pending = false;
   // storage handed out through cb_step
-  std::vector<int64_t> req_ids, evicted, admitted;
+  std::vector<int64_t> req_ids, evicted, admitted, preempted;
   std::vector<int32_t> cu, ctx, bt, slots, owner;
 };
 
@@ -93,7 +96,17 @@ extern "C" int cb_sched_set_static(cb_sched* s, int32_t batch_size) {
   if (!s || batch_size < 1) return cb::fail(CB_ERR_INVALID_ARG, "cb_sched_set_static: batch_size must be >= 1");
   if (s->has_pending || !s->running.empty())
     return cb::fail(CB_ERR_STATE, "cb_sched_set_static: requests are already running");
+  if (s->preempt) return cb::fail(CB_ERR_STATE, "cb_sched_set_static: preemption is enabled");
   s->static_b = batch_size;
+  return CB_OK;
+}
+
+extern "C" int cb_sched_set_preemption(cb_sched* s, int32_t enable, int32_t watermark_blocks) {
+  if (!s || watermark_blocks < 0)
+    return cb::fail(CB_ERR_INVALID_ARG, "cb_sched_set_preemption: watermark_blocks must be >= 0");
+  if (s->static_b > 0 && enable) return cb::fail(CB_ERR_STATE, "cb_sched_set_preemption: not with naive batching");
+  s->preempt = enable != 0;
+  s->watermark = watermark_blocks;
   return CB_OK;
 }
 
@@ -103,6 +116,7 @@ extern "C" int cb_sched_add(cb_sched* s, int64_t req_id, int32_t prompt_len, int
   Req r;
   r.id = req_id;
   r.prompt_len = prompt_len;
+  r.pre_len = prompt_len;
   r.out_len = out_len;
   s->waiting.push_back(std::move(r));
   return CB_OK;
@@ -124,6 +138,7 @@ extern "C" int cb_sched_add_cached(cb_sched* s, int64_t req_id, int32_t prompt_l
   Req r;
   r.id = req_id;
   r.prompt_len = prompt_len;
+  r.pre_len = prompt_len;
   r.out_len = out_len;
   r.ctx = cached;
   r.gen = generated;
@@ -206,6 +221,7 @@ extern "C" int cb_sched_build(cb_sched* s, cb_step* out) {
   const int32_t bs = s->bs;
   s->evicted.clear();
   s->admitted.clear();
+  s->preempted.clear();
   std::vector<std::pair<int32_t, int32_t>> batch;
   int32_t num_decode = 0;
   if (s->static_b > 0) {
@@ -230,13 +246,34 @@ extern "C" int cb_sched_build(cb_sched* s, cb_step* out) {
 
     // 2. decode-phase requests first, one token each (at most m)
     int64_t need = 0;
-    for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()); ++i) {
-      const Req& r = s->running[i];
-      if (r.ctx >= r.prompt_len) {
-        if (static_cast<int32_t>(batch.size()) == s->m) break;
-        batch.emplace_back(i, 1);
-        need += std::max<int64_t>(0, ceil_div(r.ctx + 1, bs) - static_cast<int64_t>(r.blocks.size()));
+    auto collect_decodes = [&]() {
+      batch.clear();
+      need = 0;
+      for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()); ++i) {
+        const Req& r = s->running[i];
+        if (r.ctx >= r.pre_len) {
+          if (static_cast<int32_t>(batch.size()) == s->m) break;
+          batch.emplace_back(i, 1);
+          need += std::max<int64_t>(0, ceil_div(r.ctx + 1, bs) - static_cast<int64_t>(r.blocks.size()));
+        }
       }
+    };
+    collect_decodes();
+    // Preemption (hassanahmed, paged-memory section: when the card fills, a request is
+    // evicted for a while and brought back later): the most recently admitted request gives
+    // back all its blocks and returns to the head of the waiting queue; on re-admission it
+    // prefills every token it has (prompt and generated), the last of which yields its next
+    // token, so its output continues where it stopped.
+    while (need > static_cast<int64_t>(s->free_list.size()) && s->preempt && !s->running.empty()) {
+      Req r = std::move(s->running.back());
+      s->running.pop_back();
+      for (int32_t b : r.blocks) s->free_list.push_back(b);
+      r.blocks.clear();
+      r.pre_len = r.prompt_len + r.gen;
+      r.ctx = 0;
+      s->preempted.push_back(r.id);
+      s->waiting.push_front(std::move(r));
+      collect_decodes();
     }
     if (need > static_cast<int64_t>(s->free_list.size()))
       return cb::fail(CB_ERR_OUT_OF_BLOCKS, "cb_sched_build: free list cannot hold the decode tokens");
@@ -253,9 +290,9 @@ extern "C" int cb_sched_build(cb_sched* s, cb_step* out) {
     // 3. continue partly prefilled requests
     for (int32_t i = 0; i < static_cast<int32_t>(s->running.size()) && budget > 0; ++i) {
       Req& r = s->running[i];
-      if (r.ctx >= r.prompt_len) continue;
+      if (r.ctx >= r.pre_len) continue;
       int64_t cap = (static_cast<int64_t>(r.blocks.size()) + static_cast<int64_t>(s->free_list.size())) * bs - r.ctx;
-      int64_t q = std::min<int64_t>({static_cast<int64_t>(r.prompt_len - r.ctx), budget, cap});
+      int64_t q = std::min<int64_t>({static_cast<int64_t>(r.pre_len - r.ctx), budget, cap});
       if (q <= 0) continue;
       while (static_cast<int64_t>(r.blocks.size()) < ceil_div(r.ctx + q, bs)) {
         r.blocks.push_back(s->free_list.front());
@@ -269,9 +306,9 @@ extern "C" int cb_sched_build(cb_sched* s, cb_step* out) {
     while (!s->waiting.empty() && budget > 0 &&
            (s->max_num_seqs == 0 || static_cast<int32_t>(s->running.size()) < s->max_num_seqs)) {
       Req& w = s->waiting.front();
-      int64_t q = std::min<int64_t>(w.prompt_len, budget);
+      int64_t q = std::min<int64_t>(w.pre_len, budget);
       int32_t nb = ceil_div(q, bs);
-      if (nb > static_cast<int32_t>(s->free_list.size())) break;
+      if (static_cast<int64_t>(nb) + s->watermark > static_cast<int64_t>(s->free_list.size())) break;
       Req r = std::move(w);
       s->waiting.pop_front();
       for (int32_t k = 0; k < nb; ++k) {
@@ -330,6 +367,8 @@ extern "C" int cb_sched_build(cb_sched* s, cb_step* out) {
   out->num_admitted = static_cast<int32_t>(s->admitted.size());
   out->evicted = s->evicted.data();
   out->admitted = s->admitted.data();
+  out->num_preempted = static_cast<int32_t>(s->preempted.size());
+  out->preempted = s->preempted.data();
   return CB_OK;
 }
 
@@ -339,8 +378,8 @@ extern "C" int cb_sched_commit(cb_sched* s, const uint8_t* eos) {
   for (size_t k = 0; k < s->pending.size(); ++k) {
     Req& r = s->running[s->pending[k].first];
     // a padded prefill row set (naive batching) ends at the prompt: pads hold no context
-    r.ctx = r.ctx < r.prompt_len ? std::min(r.ctx + s->pending[k].second, r.prompt_len) : r.ctx + s->pending[k].second;
-    if (r.ctx >= r.prompt_len) {      // this step produced an output token
+    r.ctx = r.ctx < r.pre_len ? std::min(r.ctx + s->pending[k].second, r.pre_len) : r.ctx + s->pending[k].second;
+    if (r.ctx >= r.pre_len) {         // this step produced an output token
       r.gen += 1;
       if (r.gen >= r.out_len || (eos && eos[k])) r.done = true;
     }

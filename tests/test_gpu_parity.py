@@ -364,3 +364,29 @@ def test_static_batching_steps(batch_size):
     for i in range(0, len(reqs), batch_size):
         expect += max(r.out_len for r in reqs[i:i + batch_size])
     assert n == expect
+
+
+def test_preemption_recompute_steps():
+    """A pool too small for every running request: preempted requests come back and prefill
+    their prompt and generated tokens again. Every row of every step matches the oracle."""
+    reqs = [W.Request(i, p, o) for i, (p, o) in enumerate([(40, 45), (25, 60), (60, 30), (18, 50), (33, 40)])]
+    wl = W.custom(reqs, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16", seed=4, token_budget=96,
+                  num_blocks=14)
+    run = DeviceRun(wl)
+    run.sched.set_preemption(True)
+    n, preempted, rows = 0, 0, 0
+    while True:
+        step = run.sched.build()
+        preempted += len(step.preempted)
+        if step.num_reqs == 0 and run.sched.stats()[:2] == (0, 0):
+            break
+        if step.num_reqs:
+            _, batch, q, k, v, o = run.run_step(step)
+            torch.cuda.synchronize()
+            check(o, oracle_full(wl, step), "bf16", f"preemption step {n} (T={step.num_tokens})")
+            rows += step.num_tokens
+        run.sched.commit()
+        n += 1
+        assert n < 2000
+    assert preempted > 0
+    assert rows > sum(r.prompt_len + r.out_len - 1 for r in reqs)

@@ -290,3 +290,80 @@ def test_static_padded_prompt_out_of_blocks():
     s.add(0, 20, 2)
     with pytest.raises(OutOfBlocks):
         s.build()
+
+
+# ---- preemption by recompute (NEXT #2) ---------------------------------------------------
+def test_preemption_victim_is_latest_and_resumes_its_output():
+    """Three decoding requests on a pool that cannot hold their next tokens: the most recently
+    admitted gives back its blocks, waits at the head of the queue, and on re-admission
+    prefills prompt + generated tokens; the last of them yields its next token."""
+    s = RefScheduler(token_budget=64, block_size=4, num_blocks=6)
+    s.set_preemption(True)
+    for rid in range(3):
+        s.add(rid, 4, 10)
+    st = s.build()                                   # three prompts of 4: 3 blocks
+    assert st.admitted == [0, 1, 2]
+    s.commit()                                        # each produced 1 token; ctx = 4
+    st = s.build()                                    # decodes need one new block each: 3 = 3 free
+    assert st.num_decode == 3 and st.preempted == []
+    s.commit()
+    for _ in range(3):                                # ctx 5..7 stay inside the second block
+        st = s.build()
+        s.commit()
+    st = s.build()                                    # ctx 8: each needs a third block, none free
+    assert st.preempted == [2] and st.req_ids.tolist() == [0, 1]
+    assert [w.req_id for w in s.waiting] == [2]
+    v = s.waiting[0]
+    assert v.ctx == 0 and v.pre_len == 4 + v.gen and v.gen == 5 and v.blocks == []
+    s.commit()
+
+
+def recompute_trace(wl, steps_limit=20000, watermark=0):
+    s = make(wl)
+    s.set_preemption(True, watermark)
+    meta = {r.req_id: r for k in range(wl.steps) for r in wl.arrivals[k]}
+    rows, extra, preempts = {}, {}, 0
+    ctx_of = {}
+    k = 0
+    while k < wl.steps or not s.idle():
+        if k < wl.steps:
+            for r in wl.arrivals[k]:
+                s.add(r.req_id, r.prompt_len, r.out_len)
+        before = {r.req_id: r.ctx for r in s.running}
+        st = s.build()
+        for rid in st.preempted:
+            extra[rid] = extra.get(rid, 0) + before[rid]
+            preempts += 1
+        q = np.diff(st.cu_q_lens)
+        for i, rid in enumerate(st.req_ids.tolist()):
+            rows[rid] = rows.get(rid, 0) + int(q[i])
+        s.commit()
+        k += 1
+        assert k < steps_limit
+    return meta, rows, extra, preempts, s
+
+
+def test_preemption_completes_every_request_with_recompute_rows():
+    """Under block pressure every request finishes; each processed prompt + out - 1 rows plus,
+    per preemption, the positions it had in the cache when it was preempted."""
+    wl = W.trace_workload(seed=8, steps=150, rate=1.0, prompt_median=30, prompt_max=120, out_mean=40,
+                          token_budget=128, num_blocks=40)
+    meta, rows, extra, preempts, s = recompute_trace(wl)
+    assert preempts > 0
+    assert s.num_free_blocks == wl.num_blocks
+    for rid, r in meta.items():
+        assert rows[rid] == r.prompt_len + r.out_len - 1 + extra.get(rid, 0), rid
+
+
+def test_preemption_watermark_keeps_blocks_free_at_admission():
+    s = RefScheduler(token_budget=64, block_size=4, num_blocks=10)
+    s.set_preemption(True, watermark_blocks=4)
+    s.add(0, 16, 3)                                   # 4 blocks, leaves 6 >= 4
+    s.add(1, 12, 3)                                   # 3 blocks would leave 3 < 4: waits
+    st = s.build()
+    assert st.admitted == [0] and s.num_free_blocks == 6
+    wl = W.trace_workload(seed=9, steps=120, rate=1.0, prompt_median=30, prompt_max=120, out_mean=30,
+                          token_budget=128, num_blocks=48)
+    meta, rows, extra, preempts, s = recompute_trace(wl, watermark=6)
+    for rid, r in meta.items():
+        assert rows[rid] == r.prompt_len + r.out_len - 1 + extra.get(rid, 0)

@@ -23,6 +23,7 @@ def pair(wl: W.Workload):
 def same_step(a, b):
     assert a.num_decode == b.num_decode
     assert a.evicted == b.evicted and a.admitted == b.admitted
+    assert list(getattr(a, "preempted", [])) == list(getattr(b, "preempted", []))
     for name in ("req_ids", "cu_q_lens", "ctx_lens", "slot_mapping", "token_to_req"):
         assert np.array_equal(getattr(a, name), getattr(b, name)), name
     assert a.block_tables.shape == b.block_tables.shape
@@ -141,3 +142,37 @@ def test_static_batching_set_after_start_is_rejected():
     lib.commit()
     with pytest.raises(cb.CbError):
         lib.set_static(4)
+
+
+@pytest.mark.parametrize("num_blocks,watermark,eos_rate", [(40, 0, 0.0), (60, 4, 0.0), (35, 0, 0.03), (900, 0, 0.0)])
+def test_preemption_matches_reference(num_blocks, watermark, eos_rate):
+    """Preemption by recompute under block pressure, step by step against the reference."""
+    wl = W.trace_workload(seed=13, steps=200, rate=1.2, prompt_median=30, prompt_max=120, out_mean=40,
+                          token_budget=128, num_blocks=num_blocks)
+    ref, lib = pair(wl)
+    ref.set_preemption(True, watermark)
+    lib.set_preemption(True, watermark)
+    rng = np.random.default_rng(num_blocks)
+    k, preempted = 0, 0
+    while k < wl.steps or not ref.idle():
+        if k < wl.steps:
+            for r in wl.arrivals[k]:
+                ref.add(r.req_id, r.prompt_len, r.out_len)
+                lib.add(r.req_id, r.prompt_len, r.out_len)
+        a, b = ref.build(), lib.build()
+        same_step(a, b)
+        preempted += len(a.preempted)
+        eos = (rng.random(a.num_reqs) < eos_rate).astype(np.uint8) if eos_rate else None
+        ref.commit(eos)
+        lib.commit(eos)
+        assert lib.stats() == (len(ref.running), len(ref.waiting), ref.num_free_blocks)
+        k += 1
+        assert k < 50000
+    assert (preempted > 0) == (num_blocks < 100)
+
+
+def test_preemption_and_static_are_exclusive():
+    lib = cb.Scheduler(64, 16, 100)
+    lib.set_static(2)
+    with pytest.raises(cb.CbError):
+        lib.set_preemption(True)
