@@ -51,7 +51,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   constexpr int ROWS = 32 * NW;                         // query rows of the work-group
   constexpr int KS = Geo::KS, VS = Geo::VS, DCH = Geo::DCH, DT = Geo::DT;
   __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
-  __shared__ int32_t lds_bt[kPrefillLdsBlocks];   // block ids of the keys this WG reads
 
   const PrefillItem it = a.items[blockIdx.x];
   if (it.req < 0) return;                                     // padding slot of the launch order
@@ -72,15 +71,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   const int wg_keys = c + min(it.q_begin + ROWS - 1, nq - 1) + 1;
   const int n_tiles = (wg_keys + kPrefillKeys - 1) / kPrefillKeys;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
-  // Stage the block ids once, so that each tile's loads depend on an LDS read rather than
-  // on a global load. Keys past kPrefillLdsBlocks*16 read the global table instead (a
-  // uniform per-tile branch).
-  const int n_bt = min((wg_keys + kBlockSize - 1) / kBlockSize, kPrefillLdsBlocks);
-  for (int i = threadIdx.x; i < n_bt; i += NT) {
-    const int blk = bt[i];
-    lds_bt[i] = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-  }
-  __syncthreads();
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
@@ -108,56 +98,57 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   constexpr int PPL = NT / TPP;                                    // pages per load
   constexpr int NL = 4 / PPL;                                      // loads per tile
   static_assert(NL * PPL == 4, "a tile is 4 pages");
-  u32x4 kreg[NL], vreg[NL];
+  // Register staging: with 8 waves (one work-group per CU) there are registers for two
+  // sets, so tiles are requested two steps before they are stored to LDS; with 4 waves one.
+  constexpr int NSET = NW == 8 ? 2 : 1;
+  u32x4 kreg[NSET][NL], vreg[NSET][NL];
   const int tl = tid % TPP;                                        // thread within its page
-  auto page_block = [&](int pidx) -> int {                         // block id of key page pidx
-    const int i = min(pidx, (wg_keys - 1) / kBlockSize);
-    int blk;
-    if (i < kPrefillLdsBlocks) {
-      blk = lds_bt[i];
-    } else {
-      blk = bt[i];
-      blk = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
-    }
-    return __builtin_amdgcn_readfirstlane(blk);
+  // Block id of key page pidx (clamped to the last page the work-group sees). The index is
+  // wave-uniform, so the id comes through the scalar cache straight into a scalar register;
+  // ids outside the pool read block 0.
+  const int last_page = __builtin_amdgcn_readfirstlane((wg_keys - 1) / kBlockSize);
+  auto page_block = [&](int pidx) -> int {
+    const int i = __builtin_amdgcn_readfirstlane(min(pidx, last_page));
+    const int blk = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(bt + i));
+    return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
   };
-  auto load_tile = [&](int j) {
+  auto load_tile = [&](int j, int set) {
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int page = u * PPL + tid / TPP;                // wave-uniform
       const int64_t base = (static_cast<int64_t>(page_block(j * 4 + page)) * hkv + g) * page_elems;
-      kreg[u] = *reinterpret_cast<const u32x4*>(kc + base + (tl / (D / 8)) * D + (tl % (D / 8)) * 8);
-      vreg[u] = *reinterpret_cast<const u32x4*>(vc + base + tl * 8);
+      kreg[set][u] = *reinterpret_cast<const u32x4*>(kc + base + (tl / (D / 8)) * D + (tl % (D / 8)) * 8);
+      vreg[set][u] = *reinterpret_cast<const u32x4*>(vc + base + tl * 8);
     }
     if ((j + 1) * kPrefillKeys > wg_keys) {        // the last tile: zero keys >= wg_keys
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const int page = u * PPL + tid / TPP;
         const int kpos = j * kPrefillKeys + page * kBlockSize + tl / (D / 8);
-        if (kpos >= wg_keys) kreg[u] = u32x4{0u, 0u, 0u, 0u};
+        if (kpos >= wg_keys) kreg[set][u] = u32x4{0u, 0u, 0u, 0u};
         const int vpos = j * kPrefillKeys + page * kBlockSize + (tl % 2) * 8;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int p0 = vpos + 2 * w;
-          vreg[u][w] &= (p0 < wg_keys ? 0x0000ffffu : 0u) | (p0 + 1 < wg_keys ? 0xffff0000u : 0u);
+          vreg[set][u][w] &= (p0 < wg_keys ? 0x0000ffffu : 0u) | (p0 + 1 < wg_keys ? 0xffff0000u : 0u);
         }
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int set) {
     uint16_t* kl = lds + buf * Geo::K_TILE;
     uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int page = u * PPL + tid / TPP;
-      *reinterpret_cast<u32x4*>(kl + (page * kBlockSize + tl / (D / 8)) * KS + (tl % (D / 8)) * 8) = kreg[u];
+      *reinterpret_cast<u32x4*>(kl + (page * kBlockSize + tl / (D / 8)) * KS + (tl % (D / 8)) * 8) = kreg[set][u];
       // Inside each 16-key page, key k sits at position (k&3) + 4*(k>>3) + 8*((k>>2)&1):
       // positions 0..7 then hold keys 0-3 and 8-11, positions 8..15 keys 4-7 and 12-15, the
       // two key sets that lanes 0-31 and 32-63 take in one 32x32x16 step (the S^T accumulator
       // layout). The thread's octet tl%2 = h (keys 8h..8h+7) goes to positions 4h.. and 8+4h..
       uint16_t* vrow = vl + (tl / 2) * VS + page * kBlockSize + (tl % 2) * 4;
-      *reinterpret_cast<u32x2*>(vrow) = u32x2{vreg[u][0], vreg[u][1]};
-      *reinterpret_cast<u32x2*>(vrow + 8) = u32x2{vreg[u][2], vreg[u][3]};
+      *reinterpret_cast<u32x2*>(vrow) = u32x2{vreg[set][u][0], vreg[set][u][1]};
+      *reinterpret_cast<u32x2*>(vrow + 8) = u32x2{vreg[set][u][2], vreg[set][u][3]};
     }
   };
 
@@ -272,27 +263,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
     }
   };
 
-  // prologue: tiles 0 and 1 in LDS, the scores of tile 0 computed, tile 2 in flight
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) load_tile(1);
+  // prologue: tiles 0 and 1 in LDS, the scores of tile 0 computed, the next NSET tiles in
+  // flight (tile t is staged in register set t % NSET)
+  load_tile(0, 0);
+  store_tile(0, 0);
+  if (n_tiles > 1) load_tile(1, 1 % NSET);
   __syncthreads();
   f32x16 sa[2], sb[2];
   if (wave_active) compute_s(0, sa);
   if (n_tiles > 1) {
-    store_tile(1);
-    if (n_tiles > 2) load_tile(2);
+    store_tile(1, 1 % NSET);
+    if (n_tiles > 2) load_tile(2, 0);
+    if (NSET == 2 && n_tiles > 3) load_tile(3, 1 % NSET);
   }
   __syncthreads();
   // Per tile j: step (reads buffer j&1, scores of j+1 from the other buffer), a barrier
-  // (buffer j&1 is free), tile j+2 from registers into it, the loads of j+3, a barrier.
+  // (buffer j&1 is free), tile j+2 from its register set into it, the loads of tile
+  // j+2+NSET into the same set, a barrier.
   // (A variant with separate key and value buffer rings and one barrier per tile measured
   // slower: the first barrier keeps the waves of the work-group in step.)
   auto advance = [&](int j) {
     __syncthreads();
     if (j + 2 < n_tiles) {
-      store_tile(j & 1);
-      if (j + 3 < n_tiles) load_tile(j + 3);
+      store_tile(j & 1, j % NSET);
+      if (j + 2 + NSET < n_tiles) load_tile(j + 2 + NSET, j % NSET);
     }
     __syncthreads();
   };

@@ -38,7 +38,6 @@ struct PrefillItem {
 
 constexpr int kBlockSize = 16;         // KV positions per physical block
 constexpr int kPrefillKeys = 64;       // keys per prefill K/V tile (4 blocks)
-constexpr int kPrefillLdsBlocks = 2048;  // block ids a prefill work-group stages in LDS
 constexpr int kMaxSplitBlocks = 64;    // blocks per decode split (one block id per lane)
 constexpr int kNumCUs = 256;           // compute units of the target GPU (MI355X)
 
