@@ -372,6 +372,16 @@ def bench_trace(args):
         ms, n = cb.cb_profile_read(kid)
         if n:
             kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "total_ms": round(ms, 3)}
+    # per-step decode efficiency (one decode launch per step that has decode rows)
+    dec_ms = cb.cb_profile_launches(cb.KERNELS["decode"])
+    step_bytes = [b for b in alg_dec_bytes[warm:warm + steps] if b > 0]
+    per_step = None
+    if len(step_bytes) == len(dec_ms) and len(dec_ms):
+        eff = np.array(step_bytes, dtype=np.float64) / (dec_ms.astype(np.float64) * 1e-3) / (HBM_PEAK_GBS * 1e9)
+        per_step = {"p10": round(float(np.percentile(eff, 10)), 4), "p50": round(float(np.percentile(eff, 50)), 4),
+                    "p90": round(float(np.percentile(eff, 90)), 4),
+                    "share_of_steps_at_or_above_0.70": round(float((eff >= 0.70).mean()), 4),
+                    "steps": int(len(eff))}
     cb.cb_profile_reset()
     T_total = int(sum(tokens[warm:warm + steps]))
     dec_bytes = int(sum(alg_dec_bytes[warm:warm + steps]))
@@ -398,7 +408,7 @@ def bench_trace(args):
                    "watermark": args.watermark if args.pool_blocks else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
-                     "traffic": None},
+                     "traffic": None, "per_step_frac": per_step},
         "device_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
         "kernels": kernels,
     }

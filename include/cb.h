@@ -187,6 +187,9 @@ enum { CB_KERNEL_APPEND = 0, CB_KERNEL_DECODE = 1, CB_KERNEL_COMBINE = 2, CB_KER
        CB_KERNEL_COUNT = 4 };
 int cb_profile_enable(int on);
 int cb_profile_read(int kernel_id, double* total_ms, int64_t* launches);
+/* Per-launch durations of one kernel id, in launch order: writes min(capacity, launches)
+ * values (ms) to host array ms_out and the number of recorded launches to *launches. */
+int cb_profile_launches(int kernel_id, float* ms_out, int64_t capacity, int64_t* launches);
 int cb_profile_reset(void);
 const char* cb_kernel_name(int kernel_id);
 

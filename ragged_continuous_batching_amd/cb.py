@@ -81,6 +81,7 @@ def _load():
         "cb_set_tuning": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
         "cb_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "cb_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), _i64p]),
+        "cb_profile_launches": (ctypes.c_int, [ctypes.c_int, P, ctypes.c_int64, _i64p]),
         "cb_profile_reset": (ctypes.c_int, []),
         "cb_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "cb_sched_create": (P, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
@@ -105,7 +106,8 @@ def _load():
 lib = _load()
 EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_attention", "cb_step_workspace_size",
             "cb_step_forward", "cb_last_error",
-            "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_reset",
+            "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
+            "cb_profile_reset",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
             "cb_sched_set_preemption")
@@ -197,6 +199,15 @@ def cb_set_tuning(key: str, value: int) -> int:
 
 def cb_profile_enable(on: bool) -> int:
     return _check(lib.cb_profile_enable(1 if on else 0))
+
+
+def cb_profile_launches(kernel_id: int) -> np.ndarray:
+    """Per-launch durations (ms) of one kernel id, in launch order."""
+    n = ctypes.c_int64()
+    _check(lib.cb_profile_launches(int(kernel_id), None, 0, ctypes.byref(n)))
+    out = np.zeros(n.value, dtype=np.float32)
+    _check(lib.cb_profile_launches(int(kernel_id), out.ctypes.data, n.value, ctypes.byref(n)))
+    return out
 
 
 def cb_profile_read(kernel_id: int):

@@ -323,7 +323,7 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
   if (split <= 0) {
     const int64_t units = total_blocks * s->num_kv_heads * p.n_sub;
     // Longer splits mean fewer partials to write and merge; the target keeps enough items
-    // to fill the machine a few times over (the matrix-core kernel runs 3 waves per SIMD,
+    // to fill the machine a few times over (the matrix-core kernel runs 2 waves per SIMD,
     // the vector-ALU one more). Measured on configs 2, 3 and the trace replay.
     const int64_t target = g_tuning.target_waves > 0 ? g_tuning.target_waves : (p.mfma_decode ? 4096 : 8192);
     split = static_cast<int32_t>(std::clamp<int64_t>((units + target - 1) / target, 4, kMaxSplitBlocks));
@@ -414,6 +414,26 @@ extern "C" int cb_profile_reset(void) {
     g_event_pool.push_back(r.stop);
   }
   g_prof.clear();
+  return CB_OK;
+}
+
+extern "C" int cb_profile_launches(int kernel_id, float* ms_out, int64_t capacity, int64_t* launches) {
+  if (kernel_id < 0 || kernel_id >= CB_KERNEL_COUNT) return fail(CB_ERR_INVALID_ARG, "bad kernel id %d", kernel_id);
+  if (capacity < 0 || (capacity > 0 && !ms_out)) return fail(CB_ERR_INVALID_ARG, "cb_profile_launches: bad buffer");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (r.kernel != kernel_id) continue;
+    if (n < capacity) {
+      if (hipEventSynchronize(r.stop) != hipSuccess) return fail(CB_ERR_HIP, "cb_profile_launches: event wait failed");
+      float ms = 0;
+      if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+        return fail(CB_ERR_HIP, "cb_profile_launches: elapsed time failed");
+      ms_out[n] = ms;
+    }
+    ++n;
+  }
+  if (launches) *launches = n;
   return CB_OK;
 }
 

@@ -24,7 +24,7 @@ namespace cb {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ __launch_bounds__(256, 3) void row_attn_mfma_kernel(RowArgs a) {
+__global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowArgs a) {
   constexpr int KC = D / 32;            // 16x16x32 steps over the head dim (scores)
   constexpr int DT = D / 16;            // 16-row output tiles over the head dim
   const int lane = lane_id();
@@ -121,15 +121,20 @@ __global__ __launch_bounds__(256, 3) void row_attn_mfma_kernel(RowArgs a) {
     }
   };
 
-  u32x4 kA[KC], kB[KC];
-  u32x2 vA[DT], vB[DT];
+  // three blocks in flight per wave (two waves per SIMD: measured slightly ahead of two
+  // blocks at three waves per SIMD)
+  u32x4 kA[KC], kB[KC], kC[KC];
+  u32x2 vA[DT], vB[DT], vC[DT];
   const int b0 = sp.blk_begin, b1 = sp.blk_end;
   load_block(b0, kA, vA);
-  for (int b = b0; b < b1; b += 2) {
-    if (b + 1 < b1) load_block(b + 1, kB, vB);
+  if (b0 + 1 < b1) load_block(b0 + 1, kB, vB);
+  for (int b = b0; b < b1; b += 3) {
+    if (b + 2 < b1) load_block(b + 2, kC, vC);
     process(b, kA, vA);
-    if (b + 2 < b1) load_block(b + 2, kA, vA);
+    if (b + 3 < b1) load_block(b + 3, kA, vA);
     if (b + 1 < b1) process(b + 1, kB, vB);
+    if (b + 4 < b1) load_block(b + 4, kB, vB);
+    if (b + 2 < b1) process(b + 2, kC, vC);
   }
 
   // each lane summed its own keys; add the other three key groups
