@@ -41,6 +41,7 @@ struct Tuning {
   int32_t decode_group = 8;       // most query heads one decode wave handles (1, 2, 4 or 8)
   int32_t decode_mfma = 1;        // 1: grouped-query decode (4+ heads per kv head) on MFMA
   int32_t stage_kernel = 1;       // 1: uploads run as a copy kernel on the stream; 0: copy engine
+  int32_t prefill_snake = 1;      // 1: alternate rounds of each XCD's prefill queue reversed
   int32_t prefill_waves = 0;      // waves per prefill work-group: 4, 8 (32 query rows each) or
                                   // 0 = 8 when that still gives two work-groups per CU, else 4
 };
@@ -311,6 +312,16 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p) {
       load[x] += grp.cost;
       queue[x].insert(queue[x].end(), grp.items.begin(), grp.items.end());
     }
+    // Within an XCD the first C = (CUs per XCD) work-groups go one to each CU, the next C
+    // take each CU's second slot in the same order, and so on. A queue sorted longest first
+    // would pair the longest first-round item with the longest second-round one; reversing
+    // every other round of C pairs long with short, so the CUs finish closer together.
+    if (g_tuning.prefill_snake) {
+      const size_t C = static_cast<size_t>(std::max(1, kNumCUs / nx));
+      for (auto& qx : queue)
+        for (size_t k0 = C; k0 < qx.size(); k0 += 2 * C)
+          std::reverse(qx.begin() + k0, qx.begin() + std::min(qx.size(), k0 + C));
+    }
     size_t depth = 0;
     for (const auto& qx : queue) depth = std::max(depth, qx.size());
     p.prefill.assign(depth * nx, PrefillItem{-1, 0, 0, 0});
@@ -378,6 +389,8 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     if (value != 0 && value != 4 && value != 8)
       return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: prefill_waves must be 0, 4 or 8");
     g_tuning.prefill_waves = value;
+  } else if (std::strcmp(key, "prefill_snake") == 0) {
+    g_tuning.prefill_snake = value != 0;
   } else if (std::strcmp(key, "stage_kernel") == 0) {
     g_tuning.stage_kernel = value != 0;
   } else if (std::strcmp(key, "decode_group") == 0) {
