@@ -136,6 +136,10 @@ def main(argv=None):
                          "continuous batching, naive padded batching (batch 32 and 8) and request-at-a-time, "
                          "all through the same kernels")
     ap.add_argument("--requests", type=int, default=256)
+    ap.add_argument("--layer", action="store_true",
+                    help="config 2 with the token-wise projections around attention (Llama-2-7B shapes, "
+                         "d_model 4096, synthetic bf16 weights): fused QKV projection + paged append, "
+                         "ragged attention, output projection")
     ap.add_argument("--pool-blocks", type=int, default=0,
                     help="config 5 only: a KV pool of this many blocks with preemption by recompute "
                          "(0 = the configured pool, which never fills)")
@@ -160,6 +164,8 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.compare_policies:
         return bench_policies(args)
+    if args.layer:
+        return bench_layer(args)
     if args.config == 5:
         return bench_trace(args)
     if args.copy_calibration:
@@ -412,6 +418,113 @@ def bench_trace(args):
         "device_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
         "kernels": kernels,
     }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_layer(args):
+    """One attention layer step on config 2's batch: x [T, 4096] -> cb_qkv_project (Q, and
+    K/V straight into the paged cache) -> cb_ragged_attention -> cb_linear (output
+    projection). The cached history is written beforehand (not timed). Throughput = rows / s;
+    the roofline line is the QKV projection (the dominant GEMM), bf16 MFMA bound."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from ragged_continuous_batching_amd import cb
+    from ragged_continuous_batching_amd.runner import DeviceRun
+
+    d_model = 4096
+    wl = W.config(2)
+    run = DeviceRun(wl, stale=None)
+    base = run.sched
+    probe = base.clone()
+    step0 = probe.build()
+    run.write_history(step0)
+    del probe
+    T = step0.num_tokens
+    hq, hkv, d = wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    n_qkv = (hq + 2 * hkv) * d
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    w_qkv = dev_bf16(W.layer_weights(wl.seed, 0, n_qkv, d_model))
+    w_o = dev_bf16(W.layer_weights(wl.seed, 1, d_model, hq * d))
+    owner = step0.token_to_req
+    rids = step0.req_ids[owner]
+    pos = step0.ctx_lens[owner] + (np.arange(T) - step0.cu_q_lens[owner])
+    x = dev_bf16(W.bf16_bits_from_f32(wl.x_values(rids, pos, d_model)))
+    q = torch.empty(T, hq, d, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    y = torch.empty(T, d_model, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(cb.cb_ragged_attention_workspace_size(run.shape, cb.Batch.from_step(step0).struct), 256),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    keep = []
+
+    def one_step():
+        s = base.clone()
+        st = s.build()
+        batch = cb.Batch.from_step(st)
+        cb.cb_qkv_project(run.shape, batch.struct, d_model, x, w_qkv, q, run.k_cache, run.v_cache, stream)
+        cb.cb_ragged_attention(run.shape, batch.struct, q, run.k_cache, run.v_cache, wl.scale, o, ws, ws.numel(),
+                               stream)
+        cb.cb_linear(T, d_model, hq * d, o.reshape(T, -1), w_o, y, stream)
+        s.commit()
+        keep.append(batch)
+        if len(keep) > 4:
+            keep.pop(0)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    cb.cb_profile_reset()
+    cb.cb_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cb.cb_profile_enable(False)
+    gemm_ms = cb.cb_profile_launches(cb.KERNELS["gemm"])
+    qkv_us = float(np.mean(gemm_ms[0::2])) * 1e3
+    out_us = float(np.mean(gemm_ms[1::2])) * 1e3
+    kernels = {}
+    for name, kid in cb.KERNELS.items():
+        ms, n = cb.cb_profile_read(kid)
+        if n:
+            kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
+    cb.cb_profile_reset()
+    qkv_flops = 2.0 * T * d_model * n_qkv
+    out_flops = 2.0 * T * (hq * d) * d_model
+    achieved = qkv_flops / (qkv_us * 1e-6) / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+    result = {
+        "metric": "attention-layer tokens/s per step (QKV projection + attention + output projection)",
+        "value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (random bf16 weights, N(0, 1/fan_in))",
+        "config": {"workload": "llama2-7b-shaped attention layer on the mixed step (64 decodes + 2x992 chunks)",
+                   "num_tokens": T, "d_model": d_model, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "kernel": "gemm_bt_kernel (QKV projection)",
+                     "traffic": None},
+        "gemm_us": {"qkv_projection": round(qkv_us, 2), "output_projection": round(out_us, 2),
+                    "output_projection_tflops": round(out_flops / (out_us * 1e-6) / 1e12, 1)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import layer as LY
+        rows = 64                                        # a bounded sample of the step's rows
+        xs = W.f32_from_bf16_bits(W.bf16_bits_from_f32(wl.x_values(rids[:rows], pos[:rows], d_model)))
+        wq = W.f32_from_bf16_bits(W.layer_weights(wl.seed, 0, n_qkv, d_model))
+        t1 = time.perf_counter()
+        LY.linear(xs, wq)
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(rows / dt, 1), "unit": "tokens/s (QKV projection only)",
+                                  "cores": os.cpu_count(), "kind": "oracle",
+                                  "sample": f"fp64 QKV projection of the first {rows} rows"}
     print(json.dumps(result), flush=True)
     return 0
 

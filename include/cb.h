@@ -145,6 +145,32 @@ int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
                     const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Token-wise layers around attention (Hugging Face blog, section "Attention": normalisation
+ * and matrix multiplications are token-wise, so they run on the packed stream unchanged;
+ * hassanahmed, selective batching batches these shape-agnostic operations).
+ *
+ * cb_linear: c[M, N] = a[M, K] w[N, K]^T. All bf16, row-major, device pointers, 16-byte
+ * aligned; fp32 accumulation, outputs rounded to nearest even. w is laid out like a torch
+ * Linear weight ([out features, in features]). N must be a multiple of 128 and K of 64, at
+ * most 1,048,576 (CB_ERR_UNSUPPORTED otherwise); M is any count of packed rows (0 is a
+ * no-op). NULL or unaligned pointers: CB_ERR_INVALID_ARG. Enqueued on `stream`; nothing is
+ * allocated and the caller owns every buffer.
+ *
+ * cb_qkv_project: the QKV projection of the packed rows with the KV append fused in
+ * (zhangchitc "continuous-batching", section "Inside the kernel": the new keys and values go
+ * into each request's cache entry before attention reads it). x [T, d_model] bf16, w_qkv
+ * [(Hq + 2 Hkv) * D, d_model] bf16 (rows: the Hq*D query features, then Hkv*D key features,
+ * then Hkv*D value features, head-major). Writes q [T, Hq, D] and, for every packed row, its
+ * key and value into the cache slot given by batch (as cb_kv_append does; rows whose block
+ * id is outside the pool are not written). bf16 only; d_model a multiple of 64 up to
+ * 1,048,576 and Hq*D, Hkv*D multiples of 128 (CB_ERR_UNSUPPORTED otherwise). Same stream
+ * semantics and metadata checks as cb_kv_append.
+ * ------------------------------------------------------------------------------------- */
+int cb_linear(int32_t M, int32_t N, int32_t K, const void* a, const void* w, void* c, void* stream);
+int cb_qkv_project(const cb_shape* shape, const cb_batch* batch, int32_t d_model, const void* x,
+                   const void* w_qkv, void* q, void* k_cache, void* v_cache, void* stream);
+
 /* Message describing the last error on this thread ("" if none). Owned by the library. */
 const char* cb_last_error(void);
 
@@ -184,7 +210,7 @@ int cb_set_tuning(const char* key, int32_t value);
  * duration and the launch count for one kernel id. cb_profile_reset() drops all records.
  * ------------------------------------------------------------------------------------- */
 enum { CB_KERNEL_APPEND = 0, CB_KERNEL_DECODE = 1, CB_KERNEL_COMBINE = 2, CB_KERNEL_PREFILL = 3,
-       CB_KERNEL_COUNT = 4 };
+       CB_KERNEL_GEMM = 4, CB_KERNEL_COUNT = 5 };
 int cb_profile_enable(int on);
 int cb_profile_read(int kernel_id, double* total_ms, int64_t* launches);
 /* Per-launch durations of one kernel id, in launch order: writes min(capacity, launches)

@@ -23,8 +23,8 @@ CB_ERR_OUT_OF_BLOCKS = -4
 CB_ERR_WORKSPACE_TOO_SMALL = -5
 CB_ERR_STATE = -6
 CB_F32, CB_BF16 = 0, 1
-CB_KERNEL_APPEND, CB_KERNEL_DECODE, CB_KERNEL_COMBINE, CB_KERNEL_PREFILL = 0, 1, 2, 3
-KERNELS = {"append": 0, "decode": 1, "combine": 2, "prefill": 3}
+CB_KERNEL_APPEND, CB_KERNEL_DECODE, CB_KERNEL_COMBINE, CB_KERNEL_PREFILL, CB_KERNEL_GEMM = 0, 1, 2, 3, 4
+KERNELS = {"append": 0, "decode": 1, "combine": 2, "prefill": 3, "gemm": 4}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -82,6 +82,9 @@ def _load():
         "cb_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "cb_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), _i64p]),
         "cb_profile_launches": (ctypes.c_int, [ctypes.c_int, P, ctypes.c_int64, _i64p]),
+        "cb_linear": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
+        "cb_qkv_project": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), ctypes.c_int32, P, P,
+                                          P, P, P, P]),
         "cb_profile_reset": (ctypes.c_int, []),
         "cb_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "cb_sched_create": (P, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
@@ -110,7 +113,7 @@ EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_att
             "cb_profile_reset",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
-            "cb_sched_set_preemption")
+            "cb_sched_set_preemption", "cb_linear", "cb_qkv_project")
 
 
 def _check(status: int) -> int:
@@ -183,6 +186,18 @@ def cb_step_forward(shape: cb_shape, num_reqs: int, num_tokens: int, max_blocks_
                                       cu, ctx, bt, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                       ctypes.c_float(scale), _ptr(o), _ptr(workspace),
                                       ctypes.c_size_t(workspace_bytes), _stream(stream)))
+
+
+def cb_linear(M: int, N: int, K: int, a, w, c, stream=None) -> int:
+    """c[M, N] = a[M, K] w[N, K]^T (bf16)."""
+    return _check(lib.cb_linear(int(M), int(N), int(K), _ptr(a), _ptr(w), _ptr(c), _stream(stream)))
+
+
+def cb_qkv_project(shape: cb_shape, batch: cb_batch, d_model: int, x, w_qkv, q, k_cache, v_cache,
+                   stream=None) -> int:
+    """QKV projection of the packed rows with the paged KV append fused in."""
+    return _check(lib.cb_qkv_project(ctypes.byref(shape), ctypes.byref(batch), int(d_model), _ptr(x), _ptr(w_qkv),
+                                     _ptr(q), _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
 
 def cb_last_error() -> str:

@@ -26,6 +26,7 @@ hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hi
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int waves, hipStream_t s);
 hipError_t launch_rows_mfma(const RowArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_stage_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s);
 
 namespace {
 
@@ -409,6 +410,7 @@ extern "C" const char* cb_kernel_name(int k) {
     case CB_KERNEL_DECODE: return "row_attn_kernel";
     case CB_KERNEL_COMBINE: return "combine_kernel";
     case CB_KERNEL_PREFILL: return "prefill_kernel";
+    case CB_KERNEL_GEMM: return "gemm_bt_kernel";
     default: return "";
   }
 }
@@ -683,4 +685,49 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_step_forward: append launch failed: %s", hipGetErrorString(e));
   return launch_attention(shape, &b, p, ws + l.plan_base, q, k_cache, v_cache, scale, o, s);
+}
+
+extern "C" int cb_linear(int32_t M, int32_t N, int32_t K, const void* a, const void* w, void* c, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 64 != 0 || K > kGemmMaxK)
+    return fail(CB_ERR_UNSUPPORTED, "cb_linear: needs M >= 0, N a multiple of 128 and K a multiple of 64 "
+                "up to %d (got %d, %d, %d)", kGemmMaxK, M, N, K);
+  if (M == 0) return CB_OK;
+  if (!a || !w || !c || !aligned16(a) || !aligned16(w) || !aligned16(c))
+    return fail(CB_ERR_INVALID_ARG, "cb_linear: tensors must be non-NULL and 16-byte aligned");
+  GemmArgs g{a, w, c, M, N, K, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    ProfScope prof(CB_KERNEL_GEMM, s);
+    e = launch_gemm(g, 0, s);
+  }
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_linear: launch failed: %s", hipGetErrorString(e));
+  return CB_OK;
+}
+
+extern "C" int cb_qkv_project(const cb_shape* shape, const cb_batch* batch, int32_t d_model, const void* x,
+                              const void* w_qkv, void* q, void* k_cache, void* v_cache, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_batch(shape, batch))) return st;
+  if (shape->dtype != CB_BF16) return fail(CB_ERR_UNSUPPORTED, "cb_qkv_project: bf16 only");
+  const int32_t qd = shape->num_q_heads * shape->head_dim, kd = shape->num_kv_heads * shape->head_dim;
+  if (d_model <= 0 || d_model % 64 != 0 || d_model > kGemmMaxK || qd % 128 != 0 || kd % 128 != 0)
+    return fail(CB_ERR_UNSUPPORTED, "cb_qkv_project: needs d_model a multiple of 64 up to %d and Hq*D, Hkv*D "
+                "multiples of 128", kGemmMaxK);
+  if (batch->num_tokens == 0) return CB_OK;
+  if (!x || !w_qkv || !q || !k_cache || !v_cache || !aligned16(x) || !aligned16(w_qkv) || !aligned16(q) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(CB_ERR_INVALID_ARG, "cb_qkv_project: tensors must be non-NULL and 16-byte aligned");
+  GemmArgs g{x, w_qkv, q, batch->num_tokens, qd + 2 * kd, d_model, k_cache, v_cache, batch->cu_q_lens,
+             batch->ctx_lens, batch->block_tables, batch->num_reqs, batch->max_blocks_per_req,
+             shape->num_q_heads, shape->num_kv_heads, shape->head_dim, shape->num_blocks};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    ProfScope prof(CB_KERNEL_GEMM, s);
+    e = launch_gemm(g, 1, s);
+  }
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_qkv_project: launch failed: %s", hipGetErrorString(e));
+  return CB_OK;
 }

@@ -91,4 +91,25 @@ struct PrefillArgs {
   int32_t touch_ahead;    // 1: pull the key tile two steps ahead toward L2
 };
 
+// Largest reduction length of the token-wise GEMM: the work-group's loads go through buffer
+// resources whose byte range (256 weight rows x K x 2 bytes) is a 32-bit count.
+constexpr int kGemmMaxK = 1 << 20;
+
+// C[M, N] = A[M, K] B[N, K]^T (bf16 in, fp32 accumulation, bf16 out). With the QKV
+// epilogue, columns [0, Hq*D) are Q rows written to `c` ([M, Hq*D]); the next Hkv*D columns
+// are K rows and the last Hkv*D are V rows, written into the paged cache at each row's slot
+// (request found from cu_q_lens, position ctx + row offset, block from the block table).
+struct GemmArgs {
+  const void* a;
+  const void* b;
+  void* c;
+  int32_t M, N, K;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* cu_q_lens;
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
+  int32_t num_reqs, max_blocks, num_q_heads, num_kv_heads, head_dim, num_blocks;
+};
+
 }  // namespace cb

@@ -161,3 +161,30 @@ def test_scale_must_be_positive():
         rc = cb.lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, sc, FAKE, FAKE,
                                         1 << 30, None)
         assert rc == cb.CB_ERR_INVALID_ARG, sc
+
+
+def test_linear_checks_shapes_and_pointers():
+    for (m, n, k) in [(4, 96, 64), (4, 128, 48), (4, 128, (1 << 20) + 64), (-1, 128, 64)]:
+        assert cb.lib.cb_linear(m, n, k, FAKE, FAKE, FAKE, None) == cb.CB_ERR_UNSUPPORTED, (m, n, k)
+    assert cb.lib.cb_linear(4, 128, 64, None, FAKE, FAKE, None) == cb.CB_ERR_INVALID_ARG
+    assert cb.lib.cb_linear(4, 128, 64, FAKE + 2, FAKE, FAKE, None) == cb.CB_ERR_INVALID_ARG
+    assert cb.lib.cb_linear(0, 128, 64, None, None, None, None) == cb.CB_OK
+
+
+def test_qkv_project_checks_shapes_and_pointers():
+    b = _batch([0, 2], [5], 1)
+    fp32 = _shape(dtype="fp32")
+    assert cb.lib.cb_qkv_project(ctypes.byref(fp32), ctypes.byref(b), 256, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == cb.CB_ERR_UNSUPPORTED
+    shape = _shape()
+    for dm in (0, 100, (1 << 20) + 64):
+        assert cb.lib.cb_qkv_project(ctypes.byref(shape), ctypes.byref(b), dm, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     None) == cb.CB_ERR_UNSUPPORTED, dm
+    narrow = _shape(num_q_heads=1, num_kv_heads=1, head_dim=64)           # Hkv*D = 64
+    assert cb.lib.cb_qkv_project(ctypes.byref(narrow), ctypes.byref(b), 256, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None) == cb.CB_ERR_UNSUPPORTED
+    assert cb.lib.cb_qkv_project(ctypes.byref(shape), ctypes.byref(b), 256, FAKE, None, FAKE, FAKE, FAKE,
+                                 None) == cb.CB_ERR_INVALID_ARG
+    empty = _batch([0], [], 0)
+    assert cb.lib.cb_qkv_project(ctypes.byref(shape), ctypes.byref(empty), 256, None, None, None, None, None,
+                                 None) == cb.CB_OK

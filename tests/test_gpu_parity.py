@@ -390,3 +390,127 @@ def test_preemption_recompute_steps():
         assert n < 2000
     assert preempted > 0
     assert rows > sum(r.prompt_len + r.out_len - 1 for r in reqs)
+
+
+# --------------------------------------------------------------------------------------
+# token-wise layers (QKV projection with the fused paged append, output projection)
+# --------------------------------------------------------------------------------------
+from oracle import layer as LY  # noqa: E402
+
+
+def bf16_tensor(values):
+    bits = W.bf16_bits_from_f32(np.asarray(values, dtype=np.float32))
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def check_rounded(got, ref, what):
+    """bf16 outputs of an fp32-accumulated product: within half an ulp of bf16 (2^-8 of the
+    magnitude) plus a small absolute slack for the fp32 accumulation."""
+    g = got.float().cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-4
+    print(f"{what}: max_abs={err.max():.3e} worst_ratio={(err / bound).max():.3f}", flush=True)
+    assert np.isfinite(g).all()
+    assert (err <= bound).all(), f"{what}: {(err > bound).sum()} elements beyond the rounding bound"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (77, 256, 192), (300, 384, 512), (1024, 128, 4096), (2048, 12288, 4096), (600, 4096, 4096)])
+def test_linear_parity(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = W.f32_from_bf16_bits(W.bf16_bits_from_f32(rng.standard_normal((M, K)).astype(np.float32)))
+    w = W.f32_from_bf16_bits(W.bf16_bits_from_f32((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32)))
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    cb.cb_linear(M, N, K, bf16_tensor(a), bf16_tensor(w), c)
+    torch.cuda.synchronize()
+    check_rounded(c, LY.linear(a, w), f"linear M={M} N={N} K={K}")
+
+
+def qkv_inputs(wl, step, d_model, history=False):
+    """Layer inputs of the step's rows (or of every request's cached history)."""
+    if history:
+        rids = np.concatenate([np.full(c, r) for r, c in zip(step.req_ids, step.ctx_lens)]).astype(np.int64)
+        pos = np.concatenate([np.arange(c) for c in step.ctx_lens]).astype(np.int64)
+    else:
+        owner = step.token_to_req
+        rids = step.req_ids[owner]
+        pos = step.ctx_lens[owner] + (np.arange(step.num_tokens) - step.cu_q_lens[owner])
+    return rids, pos, wl.x_values(rids, pos, d_model)
+
+
+def project_history(run, step, w_qkv_t, d_model):
+    """Writes every request's cached positions through the fused projection (one packed call)."""
+    wl = run.wl
+    lens = step.ctx_lens.astype(np.int32)
+    if lens.sum() == 0:
+        return
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    batch = cb.Batch(cu, np.zeros(len(lens), np.int32), step.block_tables, device=run.device)
+    _, _, x = qkv_inputs(wl, step, d_model, history=True)
+    q = torch.empty(int(cu[-1]), wl.num_q_heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+    cb.cb_qkv_project(run.shape, batch.struct, d_model, bf16_tensor(x), w_qkv_t, q, run.k_cache, run.v_cache)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1)])
+def test_qkv_project_writes_q_and_cache(hq, hkv):
+    d_model = 256
+    wl = small_workload("mixed", hq, hkv, 128, "bf16")
+    run = DeviceRun(wl)
+    step = run.sched.build()
+    n_out = (hq + 2 * hkv) * 128
+    w = W.f32_from_bf16_bits(W.layer_weights(wl.seed, 0, n_out, d_model))
+    batch = cb.Batch.from_step(step, device=run.device)
+    rids, pos, x = qkv_inputs(wl, step, d_model)
+    q = torch.empty(step.num_tokens, hq, 128, dtype=torch.bfloat16, device="cuda")
+    cb.cb_qkv_project(run.shape, batch.struct, d_model, bf16_tensor(x), bf16_tensor(w), q, run.k_cache, run.v_cache)
+    torch.cuda.synchronize()
+    qr, kr, vr = LY.qkv_split(LY.linear(x, w), hq, hkv, 128)
+    check_rounded(q.reshape(step.num_tokens, -1), qr.reshape(step.num_tokens, -1), f"qkv Q Hq={hq} Hkv={hkv}")
+    # keys and values at each row's slot (K pages [blk][g][off][d], V pages [blk][g][d][off])
+    blk = torch.from_numpy((step.slot_mapping // 16).astype(np.int64)).cuda()
+    off = torch.from_numpy((step.slot_mapping % 16).astype(np.int64)).cuda()
+    kc = run.k_cache[blk, :, off, :]
+    vc = run.v_cache[blk, :, :, off]
+    check_rounded(kc.reshape(step.num_tokens, -1), kr.reshape(step.num_tokens, -1), "qkv K pages")
+    check_rounded(vc.reshape(step.num_tokens, -1), vr.reshape(step.num_tokens, -1), "qkv V pages")
+    # slots of the step's blocks that no row wrote keep their stale fill
+    used = set(step.slot_mapping.tolist())
+    free = [b * 16 + o for b in set((step.slot_mapping // 16).tolist()) for o in range(16) if b * 16 + o not in used]
+    if free:
+        fb = torch.tensor([f // 16 for f in free], device="cuda")
+        fo = torch.tensor([f % 16 for f in free], device="cuda")
+        assert torch.isnan(run.k_cache[fb, :, fo, :].float()).all()
+
+
+def test_layer_step_end_to_end():
+    """x -> fused QKV projection (+ paged append) -> ragged attention -> output projection,
+    against the fp64 chain (no intermediate rounding) on a mixed step with cached history."""
+    hq, hkv, d, d_model = 8, 2, 128, 256
+    wl = small_workload("mixed", hq, hkv, d, "bf16")
+    run = DeviceRun(wl)
+    step = run.sched.build()
+    run._pending_history.clear()                     # history comes from the projection here
+    w_qkv = W.f32_from_bf16_bits(W.layer_weights(wl.seed, 0, (hq + 2 * hkv) * d, d_model))
+    w_o = W.f32_from_bf16_bits(W.layer_weights(wl.seed, 1, d_model, hq * d))
+    wq_t, wo_t = bf16_tensor(w_qkv), bf16_tensor(w_o)
+    project_history(run, step, wq_t, d_model)
+    batch = cb.Batch.from_step(step, device=run.device)
+    _, _, x = qkv_inputs(wl, step, d_model)
+    q = torch.empty(step.num_tokens, hq, d, dtype=torch.bfloat16, device="cuda")
+    cb.cb_qkv_project(run.shape, batch.struct, d_model, bf16_tensor(x), wq_t, q, run.k_cache, run.v_cache)
+    attn = run.attention(batch, q)
+    y = torch.empty(step.num_tokens, d_model, dtype=torch.bfloat16, device="cuda")
+    cb.cb_linear(step.num_tokens, d_model, hq * d, attn.reshape(step.num_tokens, -1), wo_t, y)
+    torch.cuda.synchronize()
+    # fp64 chain
+    qr, kr, vr = LY.qkv_split(LY.linear(x, w_qkv), hq, hkv, d)
+    _, _, xh = qkv_inputs(wl, step, d_model, history=True)
+    _, khr, vhr = LY.qkv_split(LY.linear(xh, w_qkv), hq, hkv, d) if len(xh) else (None, np.zeros((0, hkv, d)),
+                                                                                    np.zeros((0, hkv, d)))
+    hk, hv, o0 = [], [], 0
+    for c in step.ctx_lens.tolist():
+        hk.append(khr[o0:o0 + c])
+        hv.append(vhr[o0:o0 + c])
+        o0 += c
+    attn_ref = A.ragged_attention(qr, kr, vr, hk, hv, step.cu_q_lens, step.ctx_lens, wl.scale)
+    y_ref = LY.linear(attn_ref.reshape(step.num_tokens, -1), w_o)
+    check(y, y_ref, "bf16", "layer step y")

@@ -9,7 +9,10 @@ anything back into it.
 Recipe (every draw is seeded; ``seed = 1000 + config id`` for the five named workloads):
 
 * Lengths come from ``numpy.random.default_rng(seed)``, drawn in a fixed order per workload.
-* Values come from three pools (Q, K, V), each ``POOL_ROWS`` rows of ``head_dim``. Pool
+* Values come from three pools (Q, K, V), each ``POOL_ROWS`` rows of ``head_dim``; a fourth
+  (X, always bf16) holds layer inputs for the token-wise projections, a token's input row
+  being d_model / head_dim pool rows side by side. Synthetic weights are N(0, 1/fan_in)
+  from ``default_rng([seed, 100 + which])``, rounded to bf16. Pool
   ``kind`` is drawn from ``default_rng([seed, kind])`` as N(0,1) fp32, then multiplied by
   ``value_std``. For bf16 workloads it is then rounded to bf16 (round to nearest, ties to
   even).
@@ -26,7 +29,7 @@ from functools import lru_cache
 
 import numpy as np
 
-KIND_Q, KIND_K, KIND_V = 0, 1, 2
+KIND_Q, KIND_K, KIND_V, KIND_X = 0, 1, 2, 3
 _M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
 
 
@@ -133,6 +136,39 @@ class Workload:
         idx = self.index(kind, req_ids, positions)
         raw = self.raw_pool(kind)[idx]
         return f32_from_bf16_bits(raw) if self.dtype == "bf16" else raw.astype(np.float32)
+
+    # ---- layer inputs (token-wise projections around attention) ------------------------
+    def x_index(self, req_ids, positions, d_model: int) -> np.ndarray:
+        """Pool rows [N, d_model / head_dim] of the layer input of tokens (req, position)."""
+        return pool_index(self.seed, KIND_X, req_ids, positions, d_model // self.head_dim, self.pool_rows)
+
+    def x_raw_pool(self) -> np.ndarray:
+        return _x_pool(self.seed, self.pool_rows, self.head_dim, self.value_std)
+
+    def x_values(self, req_ids, positions, d_model: int) -> np.ndarray:
+        """float32 [N, d_model] layer inputs (bf16-representable): each token's row is its
+        d_model / head_dim pool rows side by side."""
+        idx = self.x_index(req_ids, positions, d_model)
+        return f32_from_bf16_bits(self.x_raw_pool()[idx]).reshape(len(idx), d_model)
+
+
+def layer_weights(seed: int, which: int, rows: int, cols: int) -> np.ndarray:
+    """bf16 bits [rows, cols] of a synthetic weight: N(0, 1/cols) from default_rng([seed,
+    100 + which]), rounded to bf16 (which: 0 = QKV projection, 1 = output projection)."""
+    g = np.random.default_rng([seed, 100 + which])
+    w = g.standard_normal((rows, cols), dtype=np.float32) * np.float32(1.0 / math.sqrt(cols))
+    return bf16_bits_from_f32(w.astype(np.float32))
+
+
+@lru_cache(maxsize=2)
+def _x_pool(seed: int, rows: int, head_dim: int, std: float):
+    g = np.random.default_rng([seed, KIND_X])
+    x = g.standard_normal((rows, head_dim), dtype=np.float32)
+    if std != 1.0:
+        x = (x * np.float32(std)).astype(np.float32)
+    out = bf16_bits_from_f32(x)
+    out.setflags(write=False)
+    return out
 
 
 @lru_cache(maxsize=4)
