@@ -144,6 +144,13 @@ def main(argv=None):
                     help="config 5 only: a KV pool of this many blocks with preemption by recompute "
                          "(0 = the configured pool, which never fills)")
     ap.add_argument("--watermark", type=int, default=0, help="blocks kept free at admission with --pool-blocks")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step as a captured HIP graph (cb_graph_step, T-bucketed); value is the "
+                         "graph's rate and the roofline kernel durations come from the eager pass of the same run "
+                         "(configs 2-4); with --config 5 the whole trace replays through graphs")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="config 5: time the replay without the library's per-kernel timing events "
+                         "(no per-kernel durations or roofline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
                          "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
@@ -284,10 +291,75 @@ def main(argv=None):
         "algorithmic": alg,
         "attention_tokens_per_s": round(T / (sum(kernels[k]["avg_us"] for k in kernels if k != "append") * 1e-6), 1),
     }
+    if args.graph:
+        result["eager"] = {"value": result["value"], "ms_per_step": result["ms_per_step"],
+                           "device_ms_per_step": result["device_ms_per_step"]}
+        result.update(bench_graph_step(args, cb, run, base, q, k_new, v_new, o, stream))
+        result["config"]["api"] = "graph"
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, step0)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_graph_step(args, cb, run, base, q, k_new, v_new, o, stream):
+    """The same step through a captured graph (bucket = T): warm-up, then K timed steps of
+    clone + build + cb_graph_step + commit, after the same loop through cb_step_forward with
+    kernel timing off (the fair eager comparison). Returns the fields that replace the eager
+    ones."""
+    import torch
+    from ragged_continuous_batching_amd.runner import GraphSteps
+
+    gs = GraphSteps(run, q, k_new, v_new, o, min_bucket=q.shape[0])
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def one_graph():
+        s = base.clone()
+        st = s.build_raw()
+        gs.step(st, stream)
+        s.commit()
+        return s
+
+    def one_eager():
+        s = base.clone()
+        st = s.build_raw()
+        need = cb.cb_step_workspace_size(run.shape, st.num_reqs, st.num_tokens, st.max_blocks_per_req,
+                                         st.cu_q_lens, st.ctx_lens)
+        nonlocal ws
+        if ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        launch_step(cb, run, st, q, k_new, v_new, o, ws, stream)
+        s.commit()
+        return s
+
+    def timed(one):
+        for _ in range(max(args.warmup, 2)):
+            one()
+        torch.cuda.synchronize()
+        keep = []
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            keep.append(one())
+            if len(keep) > 4:
+                keep.pop(0)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps
+
+    try:
+        eager_ms, _ = timed(one_eager)           # the same entry point with kernel timing off
+        ms, dev_ms = timed(one_graph)
+        stats = gs.stats()
+    finally:
+        gs.close()
+    T = q.shape[0]
+    return {"value": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "device_ms_per_step": round(dev_ms, 4),
+            "graph": {"api": "graph", "buckets": {str(b): {"replays": r, "captures": c, "workspace_bytes": w}
+                                                   for b, (r, c, w) in stats.items()},
+                      "eager_ms_per_step_without_kernel_events": round(eager_ms, 4),
+                      "roofline_from": "kernel events of the eager pass of this run (same kernels, same plan)"}}
 
 
 def bench_trace(args):
@@ -337,10 +409,20 @@ def bench_trace(args):
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sched = run.sched
+    gs = None
+    if args.graph:
+        from ragged_continuous_batching_amd.runner import GraphSteps
+        gs = GraphSteps(run, q, k_new, v_new, o, min_bucket=256)
 
     def one(kstep):
         for r in wl.arrivals[kstep]:
             sched.add(r.req_id, r.prompt_len, r.out_len)
+        if gs is not None:
+            st = sched.build_raw()
+            T = st.num_tokens
+            gs.step(st, stream)
+            sched.commit()
+            return None, T
         if args.api == "fused":
             st = sched.build_raw()
             T = st.num_tokens
@@ -360,7 +442,7 @@ def bench_trace(args):
         one(kstep)
     torch.cuda.synchronize()
     cb.cb_profile_reset()
-    cb.cb_profile_enable(True)
+    cb.cb_profile_enable(not args.no_kernel_events)
     keep = []
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -391,7 +473,16 @@ def bench_trace(args):
     cb.cb_profile_reset()
     T_total = int(sum(tokens[warm:warm + steps]))
     dec_bytes = int(sum(alg_dec_bytes[warm:warm + steps]))
-    achieved = dec_bytes / (kernels["decode"]["total_ms"] * 1e-3) / 1e9
+    graph_stats = None
+    if gs is not None:
+        graph_stats = {str(b): {"replays": r, "captures": c, "workspace_bytes": w} for b, (r, c, w) in gs.stats().items()}
+        gs.close()
+    roofline = None
+    if "decode" in kernels:
+        achieved = dec_bytes / (kernels["decode"]["total_ms"] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
+                    "traffic": None, "per_step_frac": per_step}
     result = {
         "metric": "ragged-attention tokens/s per step",
         "value": round(T_total / wall, 1),
@@ -409,15 +500,16 @@ def bench_trace(args):
                                "geometric outputs)", "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "token_budget": m,
                    "num_blocks": args.pool_blocks or wl.num_blocks, "seed": wl.seed,
-                   "tokens_timed": T_total, "api": args.api,
+                   "tokens_timed": T_total, "api": "graph" if gs is not None else args.api,
                    "preemptions_timed": int(sum(preempted[warm:warm + steps])),
                    "watermark": args.watermark if args.pool_blocks else None},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
-                     "traffic": None, "per_step_frac": per_step},
+        "roofline": roofline,
         "device_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
         "kernels": kernels,
     }
+    if graph_stats is not None:
+        result["graph"] = {"buckets": graph_stats,
+                           "roofline": "null: kernels inside a graph carry no per-kernel events"}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -146,6 +146,48 @@ int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
                     float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Captured steps (HIP graphs). Hugging Face blog "Continuous batching from first
+ * principles", section "Continuous batching": graph capture needs static tensor shapes,
+ * which a batch axis meets only by padding every prompt to one length. A cb_graph is the
+ * whole step of cb_step_forward (metadata copy, KV append, prefill tiles, split-K decode,
+ * combine) captured once and replayed for every later step whose packed rows fit its
+ * capacity (max_tokens: the caller's bucket of T). Its shapes are static capacities, not
+ * padding: the live sizes and work lists travel in a header that the replayed copy moves to
+ * the device, and work-groups past the live counts exit at once.
+ *
+ * cb_graph_create: binds the graph to fixed buffers (device pointers, 16-byte aligned):
+ *   q [max_tokens, Hq, D], k_new / v_new [max_tokens, Hkv, D], o [max_tokens, Hq, D]
+ *   and the caches, as in cb_step_forward. A step uses their first num_tokens rows. The
+ *   caller owns them and keeps them alive until cb_graph_destroy. The graph owns a device
+ *   workspace and two pinned staging buffers, sized at the first step and grown (with a
+ *   new capture) when a later step needs more. Captures on the current device; later
+ *   calls must run with the same device current. Returns CB_OK and *out, or an error
+ *   (nothing created).
+ * cb_graph_step: one step from host metadata, exactly as cb_step_forward takes it (the
+ *   same checks, CB_ERR_INVALID_ARG for num_tokens > max_tokens). Writes the header,
+ *   metadata and plan into a staging buffer, then launches the graph on `stream`. The two
+ *   staging buffers alternate; a call waits (host side) for the replay two steps back
+ *   before it reuses its buffer, so the host may build step n+1 while step n runs. Steps of
+ *   one graph must be ordered on one stream; graphs must not be shared between threads
+ *   without a lock. Results are bit-identical to cb_step_forward's on the same inputs.
+ * cb_graph_stats: replays launched, captures made (the first, then one each time a step
+ *   outgrows the capacities, which then at least double) and the workspace size in bytes;
+ *   any pointer may be NULL.
+ * cb_graph_destroy: waits for replays in flight and frees the graph (NULL is a no-op).
+ * ------------------------------------------------------------------------------------- */
+typedef struct cb_graph cb_graph;
+
+int cb_graph_create(const cb_shape* shape, int32_t max_tokens, const void* q, const void* k_new,
+                    const void* v_new, void* k_cache, void* v_cache, float scale, void* o,
+                    cb_graph** out);
+int cb_graph_step(cb_graph* graph, int32_t num_reqs, int32_t num_tokens, int32_t max_blocks_per_req,
+                  const int32_t* h_cu_q_lens, const int32_t* h_ctx_lens,
+                  const int32_t* h_block_tables, void* stream);
+int cb_graph_stats(const cb_graph* graph, int64_t* replays, int64_t* captures,
+                   size_t* workspace_bytes);
+void cb_graph_destroy(cb_graph* graph);
+
+/* ---------------------------------------------------------------------------------------
  * Token-wise layers around attention (Hugging Face blog, section "Attention": normalisation
  * and matrix multiplications are token-wise, so they run on the packed stream unchanged;
  * hassanahmed, selective batching batches these shape-agnostic operations).

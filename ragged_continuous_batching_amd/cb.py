@@ -98,6 +98,11 @@ def _load():
         "cb_sched_clone": (P, [P]),
         "cb_sched_destroy": (None, [P]),
         "cb_sched_stats": (ctypes.c_int, [P, _i32p, _i32p, _i32p]),
+        "cb_graph_create": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.c_int32, P, P, P, P, P, ctypes.c_float,
+                                           P, ctypes.POINTER(ctypes.c_void_p)]),
+        "cb_graph_step": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
+        "cb_graph_stats": (ctypes.c_int, [P, _i64p, _i64p, ctypes.POINTER(ctypes.c_size_t)]),
+        "cb_graph_destroy": (None, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -113,7 +118,8 @@ EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_att
             "cb_profile_reset",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
-            "cb_sched_set_preemption", "cb_linear", "cb_qkv_project")
+            "cb_sched_set_preemption", "cb_linear", "cb_qkv_project", "cb_graph_create", "cb_graph_step",
+            "cb_graph_stats", "cb_graph_destroy")
 
 
 def _check(status: int) -> int:
@@ -186,6 +192,33 @@ def cb_step_forward(shape: cb_shape, num_reqs: int, num_tokens: int, max_blocks_
                                       cu, ctx, bt, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                       ctypes.c_float(scale), _ptr(o), _ptr(workspace),
                                       ctypes.c_size_t(workspace_bytes), _stream(stream)))
+
+
+def cb_graph_create(shape: cb_shape, max_tokens: int, q, k_new, v_new, k_cache, v_cache, scale: float, o) -> int:
+    """Returns the cb_graph handle (an address) bound to these buffers of max_tokens rows."""
+    out = ctypes.c_void_p()
+    _check(lib.cb_graph_create(ctypes.byref(shape), int(max_tokens), _ptr(q), _ptr(k_new), _ptr(v_new),
+                               _ptr(k_cache), _ptr(v_cache), ctypes.c_float(scale), _ptr(o), ctypes.byref(out)))
+    return out.value
+
+
+def cb_graph_step(graph: int, num_reqs: int, num_tokens: int, max_blocks_per_req: int, h_cu_q_lens, h_ctx_lens,
+                  h_block_tables, stream=None) -> int:
+    """Host metadata as in cb_step_forward (numpy arrays or a cb_step's int32 pointers)."""
+    (cu, _a), (ctx, _b), (bt, _c) = _host_i32(h_cu_q_lens), _host_i32(h_ctx_lens), _host_i32(h_block_tables)
+    return _check(lib.cb_graph_step(graph, int(num_reqs), int(num_tokens), int(max_blocks_per_req), cu, ctx, bt,
+                                    _stream(stream)))
+
+
+def cb_graph_stats(graph: int):
+    """(replays, captures, workspace_bytes)."""
+    replays, captures, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check(lib.cb_graph_stats(graph, ctypes.byref(replays), ctypes.byref(captures), ctypes.byref(ws)))
+    return replays.value, captures.value, ws.value
+
+
+def cb_graph_destroy(graph: int) -> None:
+    lib.cb_graph_destroy(graph)
 
 
 def cb_linear(M: int, N: int, K: int, a, w, c, stream=None) -> int:

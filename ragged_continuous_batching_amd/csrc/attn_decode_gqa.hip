@@ -27,6 +27,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void row_attn_mfma_kernel(RowArgs a) {
   constexpr int KC = D / 32;            // 16x16x32 steps over the head dim (scores)
   constexpr int DT = D / 16;            // 16-row output tiles over the head dim
+  if (a.desc) resolve_desc(a);
   const int lane = lane_id();
   const int wave = wave_id();
   const int item = blockIdx.x * 4 + wave;

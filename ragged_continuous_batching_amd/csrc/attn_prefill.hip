@@ -52,6 +52,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_kernel(PrefillArgs a)
   constexpr int KS = Geo::KS, VS = Geo::VS, DCH = Geo::DCH, DT = Geo::DT;
   __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
 
+  if (a.desc) resolve_desc(a);
+  if (static_cast<int>(blockIdx.x) >= a.n_items) return;     // past a replayed step's items
   const PrefillItem it = a.items[blockIdx.x];
   if (it.req < 0) return;                                     // padding slot of the launch order
   const int r = it.req, h = it.head;

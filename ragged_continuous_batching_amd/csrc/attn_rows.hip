@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
   static_assert(G <= RL, "one writer lane per head");
   __shared__ __align__(16) float p_lds[4][G][kBlockSize];
 
+  if (a.desc) resolve_desc(a);
   const int lane = lane_id();
   const int wave = wave_id();
   const int item = blockIdx.x * 4 + wave;
@@ -254,6 +255,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
 // accumulates D/64 output dims.
 template <int ES, int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  if (a.desc) resolve_desc(a);
   const int item = blockIdx.x * 4 + wave_id();
   if (item >= a.n_rows * a.num_q_heads) return;
   const int lane = lane_id();

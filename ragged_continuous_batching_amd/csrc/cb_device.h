@@ -92,4 +92,50 @@ __device__ __forceinline__ int find_request(const int32_t* __restrict__ cu, int 
   return lo;
 }
 
+// A replayed step (StepDesc non-null) takes its sizes and work arrays from the header the
+// stage copy wrote at the head of the workspace; its kernels are launched for the graph's
+// capacity, so these run before the first bounds check.
+template <class T>
+__device__ __forceinline__ T* desc_array(const StepDesc* d, int64_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(const_cast<StepDesc*>(d)) + off);
+}
+
+__device__ __forceinline__ void resolve_desc(AppendArgs& a) {
+  const StepDesc* d = a.desc;
+  a.num_reqs = d->num_reqs;
+  a.num_tokens = d->num_tokens;
+  a.max_blocks = d->max_blocks;
+  a.cu_q_lens = desc_array<const int32_t>(d, d->off_cu);
+  a.ctx_lens = desc_array<const int32_t>(d, d->off_ctx);
+  a.block_tables = desc_array<const int32_t>(d, d->off_bt);
+}
+
+__device__ __forceinline__ void resolve_desc(RowArgs& a) {
+  const StepDesc* d = a.desc;
+  a.n_items = d->n_row_items;
+  a.max_blocks = d->max_blocks;
+  a.splits = desc_array<const RowSplit>(d, d->off_splits);
+  a.block_tables = desc_array<const int32_t>(d, d->off_bt);
+  a.part_o = desc_array<float>(d, d->off_part_o);
+  a.part_ml = desc_array<float>(d, d->off_part_ml);
+}
+
+__device__ __forceinline__ void resolve_desc(CombineArgs& a) {
+  const StepDesc* d = a.desc;
+  a.n_rows = d->n_combine_rows;
+  a.rows = desc_array<const CombineRow>(d, d->off_combine);
+  a.part_o = desc_array<const float>(d, d->off_part_o);
+  a.part_ml = desc_array<const float>(d, d->off_part_ml);
+}
+
+__device__ __forceinline__ void resolve_desc(PrefillArgs& a) {
+  const StepDesc* d = a.desc;
+  a.n_items = d->n_prefill;
+  a.max_blocks = d->max_blocks;
+  a.items = desc_array<const PrefillItem>(d, d->off_prefill);
+  a.cu_q_lens = desc_array<const int32_t>(d, d->off_cu);
+  a.ctx_lens = desc_array<const int32_t>(d, d->off_ctx);
+  a.block_tables = desc_array<const int32_t>(d, d->off_bt);
+}
+
 }  // namespace cb

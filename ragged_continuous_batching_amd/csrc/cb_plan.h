@@ -36,6 +36,21 @@ struct PrefillItem {
   int32_t kv_tiles;     // key tiles this item walks (used for ordering; kept for tracing)
 };
 
+// Header at the start of a captured step's workspace (cb_graph_*). The host writes it into
+// the staging slot ahead of the step's metadata and work lists. The replayed stage copy
+// reads `stage_bytes` from it, and every replayed kernel reads its sizes and its arrays
+// (offsets in bytes from this header) here rather than from launch arguments, whose grids
+// are sized for the graph's capacity: work-groups past the live count exit at once.
+struct StepDesc {
+  int64_t stage_bytes;          // bytes the stage copy moves, this header included (x16)
+  int32_t num_reqs, num_tokens, max_blocks;
+  int32_t n_row_items;          // decode waves (RowArgs::n_items)
+  int32_t n_combine_rows;       // rows merged by the combine pass
+  int32_t n_prefill;            // prefill work-groups, empty launch-order slots included
+  int64_t off_cu, off_ctx, off_bt, off_splits, off_combine, off_prefill, off_part_o, off_part_ml;
+};
+constexpr int kDescBytes = 256;        // the header's slot at the head of the workspace
+
 constexpr int kBlockSize = 16;         // KV positions per physical block
 constexpr int kPrefillKeys = 64;       // keys per prefill K/V tile (4 blocks)
 constexpr int kMaxSplitBlocks = 64;    // blocks per decode split (one block id per lane)
@@ -50,6 +65,7 @@ struct AppendArgs {
   const int32_t* ctx_lens;
   const int32_t* block_tables;
   int32_t num_reqs, num_tokens, max_blocks, num_kv_heads, num_blocks;
+  const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
 };
 
 struct RowArgs {
@@ -65,6 +81,7 @@ struct RowArgs {
   int32_t num_q_heads, num_kv_heads, max_blocks, num_blocks;
   float scale_log2;       // scale * log2(e)
   int32_t group;          // query heads per work item
+  const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
 };
 
 struct CombineArgs {
@@ -74,6 +91,7 @@ struct CombineArgs {
   const CombineRow* rows;
   int32_t n_rows;
   int32_t num_q_heads;
+  const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
 };
 
 struct PrefillArgs {
@@ -89,6 +107,7 @@ struct PrefillArgs {
   int32_t num_q_heads, num_kv_heads, max_blocks, num_blocks;
   float scale_log2;
   int32_t touch_ahead;    // 1: pull the key tile two steps ahead toward L2
+  const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
 };
 
 // Largest reduction length of the token-wise GEMM: the work-group's loads go through buffer

@@ -31,7 +31,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   __shared__ int32_t info_blk[ROWS], info_off[ROWS];
   __shared__ int32_t info_run[ROWS / VEC];
 
+  if (a.desc) resolve_desc(a);
   const int t0 = blockIdx.x * ROWS;
+  if (t0 >= a.num_tokens) return;              // past the live rows of a replayed step
   const int g0 = blockIdx.y * HEADS;
   const int tid = threadIdx.x;
   const int nrows = min(ROWS, a.num_tokens - t0);

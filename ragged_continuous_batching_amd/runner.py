@@ -50,7 +50,7 @@ class DeviceRun:
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     def _pool(self, kind):
-        raw = self.wl.raw_pool(kind)
+        raw = self.wl.raw_pool(kind).copy()          # the pools are read-only arrays
         if self.wl.dtype == "bf16":
             return torch.from_numpy(raw.view(np.int16)).to(self.device).view(torch.bfloat16)
         return torch.from_numpy(raw).to(self.device)
@@ -125,3 +125,46 @@ class DeviceRun:
         k = self.k_cache[blk, :, off, :]                      # [L, Hkv, D]
         v = self.v_cache[blk, :, :, off]                      # [L, Hkv, D]
         return k, v
+
+
+class GraphSteps:
+    """Captured steps (cb_graph) keyed by a bucket of packed rows: the smallest power of two
+    >= T, at least ``min_bucket`` and at most the buffers' row count. Every bucket's graph is
+    bound to the first rows of the same fixed buffers q, k_new, v_new, o (the caller writes
+    a step's rows there), so buckets differ only in their launch capacities.
+    """
+
+    def __init__(self, run: DeviceRun, q, k_new, v_new, o, min_bucket: int = 64):
+        self.run, self.q, self.k_new, self.v_new, self.o = run, q, k_new, v_new, o
+        self.max_rows = q.shape[0]
+        self.min_bucket = min_bucket
+        self.graphs = {}
+
+    def bucket(self, num_tokens: int) -> int:
+        b = self.min_bucket
+        while b < num_tokens:
+            b *= 2
+        return min(b, self.max_rows)
+
+    def step(self, st, stream=None) -> None:
+        """One step from a built step (``Step`` or the raw ``cb_step`` of build_raw)."""
+        T = int(st.num_tokens)
+        if T == 0:
+            return
+        b = self.bucket(T)
+        g = self.graphs.get(b)
+        if g is None:
+            g = cb.cb_graph_create(self.run.shape, b, self.q, self.k_new, self.v_new, self.run.k_cache,
+                                   self.run.v_cache, self.run.wl.scale, self.o)
+            self.graphs[b] = g
+        cb.cb_graph_step(g, st.num_reqs, T, st.max_blocks_per_req, st.cu_q_lens, st.ctx_lens, st.block_tables,
+                         stream if stream is not None else self.run.stream)
+
+    def stats(self):
+        """{bucket: (replays, captures, workspace_bytes)}."""
+        return {b: cb.cb_graph_stats(g) for b, g in sorted(self.graphs.items())}
+
+    def close(self) -> None:
+        for g in self.graphs.values():
+            cb.cb_graph_destroy(g)
+        self.graphs.clear()

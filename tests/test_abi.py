@@ -188,3 +188,31 @@ def test_qkv_project_checks_shapes_and_pointers():
     empty = _batch([0], [], 0)
     assert cb.lib.cb_qkv_project(ctypes.byref(shape), ctypes.byref(empty), 256, None, None, None, None, None,
                                  None) == cb.CB_OK
+
+
+def test_graph_entry_points_check_arguments():
+    """cb_graph_create rejects bad arguments before it touches the device; the other graph
+    calls reject a NULL graph."""
+    shape = _shape()
+    out = ctypes.c_void_p(123)
+    for args, status in [
+        ((0, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE), cb.CB_ERR_INVALID_ARG),          # max_tokens
+        ((8, FAKE, None, FAKE, FAKE, FAKE, 1.0, FAKE), cb.CB_ERR_INVALID_ARG),          # k_new NULL
+        ((8, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 1.0, FAKE), cb.CB_ERR_INVALID_ARG),      # unaligned
+        ((8, None, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE), cb.CB_ERR_INVALID_ARG),          # q NULL
+        ((8, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE), cb.CB_ERR_INVALID_ARG),          # scale
+    ]:
+        rc = cb.lib.cb_graph_create(ctypes.byref(shape), *args, ctypes.byref(out))
+        assert rc == status, cb.cb_last_error()
+        assert out.value is None                                                         # nothing created
+        out = ctypes.c_void_p(123)
+    bad = _shape(head_dim=96)
+    assert cb.lib.cb_graph_create(ctypes.byref(bad), 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE,
+                                  ctypes.byref(out)) == cb.CB_ERR_UNSUPPORTED
+    assert cb.lib.cb_graph_create(ctypes.byref(shape), 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE,
+                                  None) == cb.CB_ERR_INVALID_ARG
+    cu = np.array([0, 1], np.int32)
+    assert cb.lib.cb_graph_step(None, 1, 1, 1, cu.ctypes.data, cu.ctypes.data, cu.ctypes.data, None) == \
+        cb.CB_ERR_INVALID_ARG
+    assert cb.lib.cb_graph_stats(None, None, None, None) == cb.CB_ERR_INVALID_ARG
+    cb.lib.cb_graph_destroy(None)
