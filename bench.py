@@ -148,6 +148,8 @@ def main(argv=None):
                     help="also time the step as a captured HIP graph (cb_graph_step, T-bucketed); value is the "
                          "graph's rate and the roofline kernel durations come from the eager pass of the same run "
                          "(configs 2-4); with --config 5 the whole trace replays through graphs")
+    ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
+                    help="cb_set_tuning(KEY, VALUE) before the run (repeatable)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="config 5: time the replay without the library's per-kernel timing events "
                          "(no per-kernel durations or roofline)")
@@ -169,6 +171,9 @@ def main(argv=None):
     from ragged_continuous_batching_amd.runner import DeviceRun
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    for kv in args.tune:
+        key, val = kv.split("=")
+        cb.cb_set_tuning(key, int(val))
     if args.compare_policies:
         return bench_policies(args)
     if args.layer:
