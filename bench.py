@@ -258,8 +258,15 @@ def main(argv=None):
     cb.cb_profile_reset()
 
     dominant = "prefill" if args.config == 4 else "decode"
+    if dominant == "decode" and "mixed" in kernels:
+        dominant = "mixed"                 # prefill tiles and decode waves in one launch
     avg_s = kernels[dominant]["avg_us"] * 1e-6
-    if dominant == "decode":
+    if dominant == "mixed":
+        achieved = alg["all"]["bytes"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "mfma_frac": round(alg["prefill"]["flops"] / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    elif dominant == "decode":
         achieved = alg["decode"]["bytes"] / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
@@ -395,7 +402,7 @@ def bench_trace(args):
     o = torch.empty_like(q)
     # dry run of the schedule on a copy: the largest workspace any step needs
     dry = run.sched.clone()
-    need, alg_dec_bytes, tokens, preempted = 0, [], [], []
+    need, alg_dec_bytes, alg_pre_bytes, both, tokens, preempted = 0, [], [], [], [], []
     for kstep in range(total_steps):
         for r in wl.arrivals[kstep]:
             dry.add(r.req_id, r.prompt_len, r.out_len)
@@ -408,6 +415,8 @@ def bench_trace(args):
                                              st.cu_q_lens, st.ctx_lens))
         alg = algorithmic(wl, st)
         alg_dec_bytes.append(alg["decode"]["bytes"])
+        alg_pre_bytes.append(alg["prefill"]["bytes"])
+        both.append(alg["decode"]["tokens"] > 0 and alg["prefill"]["tokens"] > 0)
         tokens.append(st.num_tokens)
         dry.commit()
     del dry
@@ -465,12 +474,24 @@ def bench_trace(args):
         ms, n = cb.cb_profile_read(kid)
         if n:
             kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "total_ms": round(ms, 3)}
-    # per-step decode efficiency (one decode launch per step that has decode rows)
-    dec_ms = cb.cb_profile_launches(cb.KERNELS["decode"])
-    step_bytes = [b for b in alg_dec_bytes[warm:warm + steps] if b > 0]
+    # Per-step efficiency of the launch that streams the cache: the decode kernel, or the
+    # mixed launch (prefill tiles and decode waves together; its bytes are both parts') when
+    # the step has both kinds of rows and the mixed launch is on.
+    mixed = "mixed" in kernels
+    dec_ms = [float(x) for x in cb.cb_profile_launches(cb.KERNELS["decode"])]
+    mix_ms = [float(x) for x in cb.cb_profile_launches(cb.KERNELS["mixed"])]
+    step_bytes, step_ms = [], []
     per_step = None
-    if len(step_bytes) == len(dec_ms) and len(dec_ms):
-        eff = np.array(step_bytes, dtype=np.float64) / (dec_ms.astype(np.float64) * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    for k in range(warm, warm + steps):
+        if mixed and both[k]:
+            if mix_ms:
+                step_bytes.append(alg_dec_bytes[k] + alg_pre_bytes[k])
+                step_ms.append(mix_ms.pop(0))
+        elif alg_dec_bytes[k] > 0 and dec_ms:
+            step_bytes.append(alg_dec_bytes[k])
+            step_ms.append(dec_ms.pop(0))
+    if step_ms and not dec_ms and not mix_ms:
+        eff = np.array(step_bytes, dtype=np.float64) / (np.array(step_ms, dtype=np.float64) * 1e-3) / (HBM_PEAK_GBS * 1e9)
         per_step = {"p10": round(float(np.percentile(eff, 10)), 4), "p50": round(float(np.percentile(eff, 50)), 4),
                     "p90": round(float(np.percentile(eff, 90)), 4),
                     "share_of_steps_at_or_above_0.70": round(float((eff >= 0.70).mean()), 4),
@@ -483,10 +504,11 @@ def bench_trace(args):
         graph_stats = {str(b): {"replays": r, "captures": c, "workspace_bytes": w} for b, (r, c, w) in gs.stats().items()}
         gs.close()
     roofline = None
-    if "decode" in kernels:
-        achieved = dec_bytes / (kernels["decode"]["total_ms"] * 1e-3) / 1e9
+    if step_ms:
+        achieved = sum(step_bytes) / (sum(step_ms) * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": "row_attn_mfma_kernel",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "kernel": "mixed_attn_kernel + row_attn_mfma_kernel" if mixed else "row_attn_mfma_kernel",
                     "traffic": None, "per_step_frac": per_step}
     result = {
         "metric": "ragged-attention tokens/s per step",

@@ -242,6 +242,13 @@ const char* cb_version(void);
  *   "prefill_waves"  waves per bf16 prefill work-group: 4 (128 query rows, two work-groups
  *                    per CU), 8 (256 rows, one per CU), or 0 (default) = 8 when a step has at
  *                    least 2 x 256 such work-groups, else 4
+ *   "mixed_launch"   1: a bf16 step with both prefill rows and grouped-query decode rows
+ *                    (Hq/Hkv >= 4) runs its prefill tiles (128-row work-groups) and decode
+ *                    waves in one launch, interleaved so that both kinds share every CU;
+ *                    0: two launches. Steps taken by cb_graph_step always use two launches.
+ *   "mixed_order"    order of the mixed launch: 0 (default) spreads prefill and decode
+ *                    work-groups in proportion to their counts; 1 alternates them until one
+ *                    kind runs out
  * Returns CB_ERR_INVALID_ARG for an unknown key or a negative value. */
 int cb_set_tuning(const char* key, int32_t value);
 
@@ -252,7 +259,7 @@ int cb_set_tuning(const char* key, int32_t value);
  * duration and the launch count for one kernel id. cb_profile_reset() drops all records.
  * ------------------------------------------------------------------------------------- */
 enum { CB_KERNEL_APPEND = 0, CB_KERNEL_DECODE = 1, CB_KERNEL_COMBINE = 2, CB_KERNEL_PREFILL = 3,
-       CB_KERNEL_GEMM = 4, CB_KERNEL_COUNT = 5 };
+       CB_KERNEL_GEMM = 4, CB_KERNEL_MIXED = 5, CB_KERNEL_COUNT = 6 };
 int cb_profile_enable(int on);
 int cb_profile_read(int kernel_id, double* total_ms, int64_t* launches);
 /* Per-launch durations of one kernel id, in launch order: writes min(capacity, launches)

@@ -23,8 +23,8 @@ CB_ERR_OUT_OF_BLOCKS = -4
 CB_ERR_WORKSPACE_TOO_SMALL = -5
 CB_ERR_STATE = -6
 CB_F32, CB_BF16 = 0, 1
-CB_KERNEL_APPEND, CB_KERNEL_DECODE, CB_KERNEL_COMBINE, CB_KERNEL_PREFILL, CB_KERNEL_GEMM = 0, 1, 2, 3, 4
-KERNELS = {"append": 0, "decode": 1, "combine": 2, "prefill": 3, "gemm": 4}
+CB_KERNEL_APPEND, CB_KERNEL_DECODE, CB_KERNEL_COMBINE, CB_KERNEL_PREFILL, CB_KERNEL_GEMM, CB_KERNEL_MIXED = 0, 1, 2, 3, 4, 5
+KERNELS = {"append": 0, "decode": 1, "combine": 2, "prefill": 3, "gemm": 4, "mixed": 5}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)

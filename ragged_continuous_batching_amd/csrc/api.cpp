@@ -28,6 +28,7 @@ hipError_t launch_rows_mfma(const RowArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_stage_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_stage_copy_desc(const void* src, void* dst, size_t max_bytes, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s);
+hipError_t launch_mixed(const MixedArgs& a, int head_dim, hipStream_t s);
 
 namespace {
 
@@ -46,6 +47,9 @@ struct Tuning {
   int32_t prefill_snake = 1;      // 1: alternate rounds of each XCD's prefill queue reversed
   int32_t prefill_waves = 0;      // waves per prefill work-group: 4, 8 (32 query rows each) or
                                   // 0 = 8 when that still gives two work-groups per CU, else 4
+  int32_t mixed_launch = 0;       // 1: prefill tiles and matrix-core decode waves in one launch
+  int32_t mixed_order = 0;        // 0: merge prefill and decode chunks in proportion to their
+                                  // counts; 1: alternate them until one kind runs out
 };
 Tuning g_tuning;
 
@@ -239,11 +243,30 @@ struct Plan {
   bool mfma_decode = false;  // decode rows on the MFMA kernel
   int prefill_waves = 4;     // waves (x 32 query rows) per prefill work-group
   int n_sub = 1;         // decode waves per kv head
-  size_t off_combine = 0, off_prefill = 0, plan_bytes = 0, off_part_o = 0, off_part_ml = 0, total = 0;
+  bool mixed = false;    // prefill tiles and decode waves in one launch (order below)
+  std::vector<int32_t> order;
+  size_t off_combine = 0, off_prefill = 0, off_order = 0, plan_bytes = 0, off_part_o = 0, off_part_ml = 0,
+         total = 0;
 };
 
+// Would a step with these rows take the mixed launch? bf16 steps with prefill chunks and
+// matrix-core decode rows (the 4-wave prefill work-group then has the decode work-group's
+// shape, and both fit two to a CU).
+bool wants_mixed(const cb_shape* s, const cb_batch* b) {
+  if (!g_tuning.mixed_launch || s->dtype != CB_BF16 || !g_tuning.decode_mfma) return false;
+  if (s->num_q_heads / s->num_kv_heads < 4) return false;
+  bool dec = false, pre = false;
+  for (int32_t r = 0; r < b->num_reqs; ++r) {
+    const int32_t q = b->h_cu_q_lens[r + 1] - b->h_cu_q_lens[r];
+    dec |= q == 1;
+    pre |= q > 1;
+  }
+  return dec && pre;
+}
+
 // force_waves (4 or 8) fixes the prefill work-group size; 0 takes the tuning / automatic choice.
-void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 0) {
+// allow_mixed = false keeps prefill and decode in separate launches (captured steps).
+void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 0, bool allow_mixed = true) {
   const int q_per_kv = s->num_q_heads / s->num_kv_heads;
   // query heads per decode wave: all heads of the group up to decode_group; a larger group
   // is covered by n_sub waves on adjacent slots, which read the same pages back to back
@@ -256,7 +279,8 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
   }
   p.n_sub = q_per_kv / p.group;
   const bool mfma_prefill = s->dtype == CB_BF16;
-  p.prefill_waves = force_waves ? force_waves : g_tuning.prefill_waves;
+  p.mixed = allow_mixed && wants_mixed(s, b);
+  p.prefill_waves = p.mixed ? 4 : force_waves ? force_waves : g_tuning.prefill_waves;
   if (p.prefill_waves == 0) {
     // 256-row work-groups read each key/value tile once for twice the rows, but a CU holds
     // only one of them (registers); take them when there are enough to fill every CU twice
@@ -356,10 +380,34 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
     p.n_parts += ns;
   }
 
+  if (p.mixed) {
+    // Chunks of one work-group per XCD. mixed_order 0: prefill and decode chunks merged in
+    // proportion to their counts, so prefill work-groups stay a minority of each CU's
+    // slots throughout (the cache stream, the step's bound, keeps most of them; measured on
+    // the trace replay: 594 us for the launch vs 621 us for the two kernels). mixed_order 1:
+    // alternate until one kind runs out (half the slots go to prefill: 678 us). A prefill
+    // chunk keeps the XCD positions its planner chose (the prefill list is laid out in
+    // chunks of nx); the last decode chunk is padded with work-group indices past the
+    // decode items.
+    const int nx = std::max(1, g_tuning.xcds);
+    const int64_t n_rows = static_cast<int64_t>(p.splits.size()) * s->num_kv_heads * p.n_sub;
+    const int64_t n_dwg = (n_rows + 3) / 4;
+    const int64_t pch = static_cast<int64_t>(p.prefill.size()) / nx, dch = (n_dwg + nx - 1) / nx;
+    int64_t pc = 0, dc = 0;
+    p.order.reserve(static_cast<size_t>((pch + dch) * nx));
+    while (pc < pch || dc < dch) {
+      const bool take_p = dc == dch || (pc < pch && (g_tuning.mixed_order ? pc <= dc : pc * dch <= dc * pch));
+      for (int k = 0; k < nx; ++k)
+        p.order.push_back(take_p ? static_cast<int32_t>(pc * nx + k) : static_cast<int32_t>(-1 - (dc * nx + k)));
+      (take_p ? pc : dc) += 1;
+    }
+  }
+
   const size_t eb = 4;
   p.off_combine = align256(p.splits.size() * sizeof(RowSplit));
   p.off_prefill = p.off_combine + align256(p.combine.size() * sizeof(CombineRow));
-  p.plan_bytes = p.off_prefill + p.prefill.size() * sizeof(PrefillItem);
+  p.off_order = p.off_prefill + align256(p.prefill.size() * sizeof(PrefillItem));
+  p.plan_bytes = p.off_order + p.order.size() * sizeof(int32_t);
   p.off_part_o = align256(p.plan_bytes);
   p.off_part_ml = p.off_part_o + align256(static_cast<size_t>(p.n_parts) * s->num_q_heads * s->head_dim * eb);
   p.total = p.off_part_ml + align256(static_cast<size_t>(p.n_parts) * s->num_q_heads * 2 * eb);
@@ -394,6 +442,10 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.prefill_waves = value;
   } else if (std::strcmp(key, "prefill_snake") == 0) {
     g_tuning.prefill_snake = value != 0;
+  } else if (std::strcmp(key, "mixed_launch") == 0) {
+    g_tuning.mixed_launch = value != 0;
+  } else if (std::strcmp(key, "mixed_order") == 0) {
+    g_tuning.mixed_order = value != 0;
   } else if (std::strcmp(key, "stage_kernel") == 0) {
     g_tuning.stage_kernel = value != 0;
   } else if (std::strcmp(key, "decode_group") == 0) {
@@ -413,6 +465,7 @@ extern "C" const char* cb_kernel_name(int k) {
     case CB_KERNEL_COMBINE: return "combine_kernel";
     case CB_KERNEL_PREFILL: return "prefill_kernel";
     case CB_KERNEL_GEMM: return "gemm_bt_kernel";
+    case CB_KERNEL_MIXED: return "mixed_attn_kernel";
     default: return "";
   }
 }
@@ -520,30 +573,37 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
   // more than the overlap saved.
   hipStream_t ps = s;
   SideStream* side = nullptr;
-  const bool fork = g_tuning.overlap_prefill && !p.prefill.empty() && !p.splits.empty();
+  const bool fork = g_tuning.overlap_prefill && !p.mixed && !p.prefill.empty() && !p.splits.empty();
   if (fork) {
     if ((st = side_stream(&side))) return st;
     ps = side->stream;
     if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(ps, side->fork, 0) != hipSuccess)
       return fail(CB_ERR_HIP, "cb_ragged_attention: fork failed");
   }
-  if (!p.prefill.empty()) {
-    PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
-                   batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
+  const PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
+                       batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
+                       shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks,
+                       scale_log2, g_tuning.prefill_touch};
+  const RowArgs ra{q, k_cache, v_cache, o,
+                   reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml),
+                   reinterpret_cast<const RowSplit*>(ws), batch->block_tables,
+                   static_cast<int32_t>(p.splits.size()) * shape->num_kv_heads * p.n_sub,
                    shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2,
-                   g_tuning.prefill_touch};
-    ProfScope prof(CB_KERNEL_PREFILL, ps);
-    e = launch_prefill(pa, shape->head_dim, p.prefill_waves, ps);
-  }
-  if (e == hipSuccess && !p.splits.empty()) {
-    RowArgs ra{q, k_cache, v_cache, o,
-               reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml),
-               reinterpret_cast<const RowSplit*>(ws), batch->block_tables,
-               static_cast<int32_t>(p.splits.size()) * shape->num_kv_heads * p.n_sub,
-               shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks, scale_log2,
-               p.group};
-    ProfScope prof(CB_KERNEL_DECODE, s);
-    e = p.mfma_decode ? launch_rows_mfma(ra, shape->head_dim, s) : launch_rows(ra, eb, shape->head_dim, p.group, s);
+                   p.group};
+  if (p.mixed) {
+    const MixedArgs ma{pa, ra, reinterpret_cast<const int32_t*>(ws + p.off_order),
+                       static_cast<int32_t>(p.order.size())};
+    ProfScope prof(CB_KERNEL_MIXED, s);
+    e = launch_mixed(ma, shape->head_dim, s);
+  } else {
+    if (!p.prefill.empty()) {
+      ProfScope prof(CB_KERNEL_PREFILL, ps);
+      e = launch_prefill(pa, shape->head_dim, p.prefill_waves, ps);
+    }
+    if (e == hipSuccess && !p.splits.empty()) {
+      ProfScope prof(CB_KERNEL_DECODE, s);
+      e = p.mfma_decode ? launch_rows_mfma(ra, shape->head_dim, s) : launch_rows(ra, eb, shape->head_dim, p.group, s);
+    }
   }
   if (e == hipSuccess && !p.combine.empty()) {
     CombineArgs ca{o, reinterpret_cast<const float*>(ws + p.off_part_o),
@@ -567,6 +627,7 @@ void write_plan(const Plan& p, char* out) {
   if (!p.combine.empty()) std::memcpy(out + p.off_combine, p.combine.data(), p.combine.size() * sizeof(CombineRow));
   if (!p.prefill.empty())
     std::memcpy(out + p.off_prefill, p.prefill.data(), p.prefill.size() * sizeof(PrefillItem));
+  if (!p.order.empty()) std::memcpy(out + p.off_order, p.order.data(), p.order.size() * sizeof(int32_t));
 }
 
 int check_tensors(const void* q, const void* k_cache, const void* v_cache, void* o, float scale, const char* fn) {
@@ -1024,7 +1085,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
                             "cb_graph_step")))
     return st;
   Plan p;
-  make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0);
+  make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0, false);
   const GraphLayout l = graph_layout(num_reqs, max_blocks_per_req, p);
   const bool fits = g->captured && l.stage_bytes <= g->cap_stage && l.total <= g->ws_bytes &&
                     p.mfma_decode == g->mfma_decode && p.group == g->group && g_tuning.prefill_touch == g->touch;

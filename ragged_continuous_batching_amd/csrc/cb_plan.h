@@ -110,6 +110,17 @@ struct PrefillArgs {
   const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
 };
 
+// One launch holding a step's prefill tiles and its matrix-core decode waves (4-wave
+// work-groups of both kinds). order[b] >= 0: work-group b is prefill slot order[b];
+// order[b] < 0: it is decode work-group -1 - order[b] (its waves take items 4w..4w+3;
+// indices past the decode items exit at once).
+struct MixedArgs {
+  PrefillArgs prefill;
+  RowArgs decode;
+  const int32_t* order;
+  int32_t n_blocks;
+};
+
 // Largest reduction length of the token-wise GEMM: the work-group's loads go through buffer
 // resources whose byte range (256 weight rows x K x 2 bytes) is a 32-bit count.
 constexpr int kGemmMaxK = 1 << 20;

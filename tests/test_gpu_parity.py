@@ -514,3 +514,63 @@ def test_layer_step_end_to_end():
     attn_ref = A.ragged_attention(qr, kr, vr, hk, hv, step.cu_q_lens, step.ctx_lens, wl.scale)
     y_ref = LY.linear(attn_ref.reshape(step.num_tokens, -1), w_o)
     check(y, y_ref, "bf16", "layer step y")
+
+
+# --------------------------------------------------------------------------------------
+# prefill tiles and grouped-query decode waves in one launch ("mixed_launch")
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,hq,hkv,d,order", [("mixed", 8, 2, 128, 0), ("mixed", 16, 2, 128, 0),
+                                                 ("tile_edges", 16, 4, 128, 0), ("long_decode", 32, 2, 128, 0),
+                                                 ("mixed", 8, 1, 64, 0), ("mixed", 64, 8, 128, 0),
+                                                 ("mixed", 16, 2, 128, 1), ("tile_edges", 16, 4, 128, 1)])
+def test_mixed_launch_matches_two_launches_and_oracle(name, hq, hkv, d, order):
+    """The mixed launch runs the same tile and wave code as the two kernels (with 128-row
+    prefill work-groups), so its output is bit-identical, in either work-group order; and
+    it matches the oracle."""
+    wl = small_workload(name, hq, hkv, d, "bf16")
+    outs = []
+    try:
+        cb.cb_set_tuning("prefill_waves", 4)
+        cb.cb_set_tuning("mixed_order", order)
+        for mixed in (0, 1):
+            cb.cb_set_tuning("mixed_launch", mixed)
+            cb.cb_profile_reset()
+            cb.cb_profile_enable(True)
+            run, step, batch, o = run_one_step(wl)
+            cb.cb_profile_enable(False)
+            launched = {k: cb.cb_profile_read(v)[1] for k, v in cb.KERNELS.items()}
+            assert launched["mixed"] == mixed and launched["prefill"] == 1 - mixed, launched
+            outs.append(o)
+    finally:
+        cb.cb_profile_enable(False)
+        cb.cb_profile_reset()
+        cb.cb_set_tuning("mixed_launch", 0)
+        cb.cb_set_tuning("mixed_order", 0)
+        cb.cb_set_tuning("prefill_waves", 0)
+    assert torch.equal(outs[0], outs[1])
+    check(outs[1], oracle_full(wl, step), "bf16", f"mixed launch {name} Hq={hq} Hkv={hkv} D={d}")
+
+
+def test_mixed_launch_trace_replay():
+    """The first 150 steps of the scheduler trace with the mixed launch; sampled rows of
+    every 30th step against the oracle."""
+    wl = W.config(5)
+    run = DeviceRun(wl, stale=None)
+    rng = np.random.default_rng(15)
+    cb.cb_set_tuning("mixed_launch", 1)
+    checked = 0
+    try:
+        for k in range(150):
+            for r in wl.arrivals[k]:
+                run.sched.add(r.req_id, r.prompt_len, r.out_len)
+            step, batch, q, kn, vn, o = run.run_step()
+            if k % 30 == 29:
+                torch.cuda.synchronize()
+                cand = sample_rows(step, 2, rng)
+                rows, ref = oracle_rows(wl, step, rng.choice(cand, size=min(64, len(cand)), replace=False))
+                check(o[torch.from_numpy(rows).cuda()], ref, "bf16", f"mixed trace step {k} (T={step.num_tokens})")
+                checked += 1
+            run.sched.commit()
+    finally:
+        cb.cb_set_tuning("mixed_launch", 0)
+    assert checked == 5
