@@ -61,8 +61,8 @@ def source_sha(*names):
 
 
 KERNEL_SOURCES = {"row_attn_kernel": ("attn_rows.hip", "cb_device.h", "cb_plan.h"),
-                  "row_attn_mfma_kernel": ("attn_decode_gqa.hip", "cb_device.h", "cb_plan.h"),
-                  "prefill_kernel": ("attn_prefill.hip", "cb_device.h", "cb_plan.h")}
+                  "row_attn_mfma_kernel": ("attn_decode_gqa.hip", "attn_decode_gqa.h", "cb_device.h", "cb_plan.h"),
+                  "prefill_kernel": ("attn_prefill.hip", "attn_prefill.h", "cb_device.h", "cb_plan.h")}
 
 
 def measured_traffic(kernel, workload):

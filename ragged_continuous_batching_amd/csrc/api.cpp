@@ -639,20 +639,36 @@ int check_tensors(const void* q, const void* k_cache, const void* v_cache, void*
 }
 
 // Workspace layout of cb_step_forward: the step metadata (cu_q_lens, ctx_lens,
-// block_tables), then the attention plan and partials at `plan_base`.
+// block_tables, then each packed row's cache slot), then the attention plan and partials at
+// `plan_base`.
 struct StepLayout {
-  size_t off_cu = 0, off_ctx = 0, off_bt = 0, meta_bytes = 0, plan_base = 0;
+  size_t off_cu = 0, off_ctx = 0, off_bt = 0, off_slots = 0, meta_bytes = 0, plan_base = 0;
 };
 
-StepLayout step_layout(int32_t R, int32_t maxb) {
+StepLayout step_layout(int32_t R, int32_t maxb, int32_t T) {
   StepLayout l;
   l.off_cu = 0;
   l.off_ctx = static_cast<size_t>(R + 1) * 4;
   l.off_bt = l.off_ctx + static_cast<size_t>(R) * 4;
-  l.meta_bytes = l.off_bt + static_cast<size_t>(R) * maxb * 4;
+  l.off_slots = l.off_bt + static_cast<size_t>(R) * maxb * 4;
+  l.meta_bytes = l.off_slots + static_cast<size_t>(std::max(T, 0)) * 4;
   l.plan_base = align256(l.meta_bytes);
   return l;
 }
+
+// Cache slot (block * block_size + offset) of every packed row, from the host metadata
+// (the slot rule of cb_kv_append: row i of request r sits at position ctx_lens[r] + i).
+// Block ids were checked against the pool before this is called.
+void fill_slots(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt, int32_t* out) {
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t* row = bt + static_cast<size_t>(r) * maxb;
+    for (int32_t t = cu[r], p = ctx[r]; t < cu[r + 1]; ++t, ++p) out[t] = row[p / kBlockSize] * kBlockSize + p % kBlockSize;
+  }
+}
+
+// Slots fit an int32 for every pool this library accepts in practice; larger pools keep the
+// device-side lookup.
+inline bool slots_fit(const cb_shape* s) { return s->num_blocks <= INT32_MAX / kBlockSize; }
 
 }  // namespace
 }  // namespace cb
@@ -708,7 +724,7 @@ extern "C" size_t cb_step_workspace_size(const cb_shape* shape, int32_t num_reqs
                                          int32_t max_blocks_per_req, const int32_t* h_cu_q_lens,
                                          const int32_t* h_ctx_lens) {
   if (check_shape(shape) || num_reqs < 0 || max_blocks_per_req < 0) return 0;
-  const StepLayout l = step_layout(num_reqs, max_blocks_per_req);
+  const StepLayout l = step_layout(num_reqs, max_blocks_per_req, num_tokens);
   cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr, l);
   if (check_batch(shape, &b) || num_tokens == 0) return 0;
   Plan p;
@@ -723,7 +739,7 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   int st = check_shape(shape);
   if (st) return st;
   if (num_reqs < 0 || max_blocks_per_req < 0) return fail(CB_ERR_INVALID_ARG, "cb_step_forward: negative count");
-  const StepLayout l = step_layout(num_reqs, max_blocks_per_req);
+  const StepLayout l = step_layout(num_reqs, max_blocks_per_req, num_tokens);
   char* ws = static_cast<char*>(workspace);
   cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, ws, l);
   if ((st = check_batch(shape, &b))) return st;
@@ -747,12 +763,16 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
     std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
     std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
     std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
+    if (slots_fit(shape))
+      fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
+                 reinterpret_cast<int32_t*>(host + l.off_slots));
     write_plan(p, host + l.plan_base);
   });
   if (st) return st;
 
   AppendArgs aa{k_new, v_new, k_cache, v_cache, b.cu_q_lens, b.ctx_lens, b.block_tables, num_reqs, num_tokens,
-                max_blocks_per_req, shape->num_kv_heads, shape->num_blocks};
+                max_blocks_per_req, shape->num_kv_heads, shape->num_blocks, nullptr,
+                slots_fit(shape) ? reinterpret_cast<const int32_t*>(ws + l.off_slots) : nullptr};
   hipError_t e;
   {
     ProfScope prof(CB_KERNEL_APPEND, s);
@@ -872,15 +892,16 @@ void retire_pinned(void* p) {
 // Byte layout of a replayed step: header, metadata, then the plan at plan_base (plan offsets
 // are relative to it). The stage copy moves [0, stage_bytes).
 struct GraphLayout {
-  size_t off_cu = 0, off_ctx = 0, off_bt = 0, plan_base = 0, stage_bytes = 0, total = 0;
+  size_t off_cu = 0, off_ctx = 0, off_bt = 0, off_slots = 0, plan_base = 0, stage_bytes = 0, total = 0;
 };
 
-GraphLayout graph_layout(int32_t R, int32_t maxb, const Plan& p) {
+GraphLayout graph_layout(int32_t R, int32_t maxb, int32_t T, const Plan& p) {
   GraphLayout l;
   l.off_cu = kDescBytes;
   l.off_ctx = l.off_cu + static_cast<size_t>(R + 1) * 4;
   l.off_bt = l.off_ctx + static_cast<size_t>(R) * 4;
-  l.plan_base = align256(l.off_bt + static_cast<size_t>(R) * maxb * 4);
+  l.off_slots = l.off_bt + static_cast<size_t>(R) * maxb * 4;
+  l.plan_base = align256(l.off_slots + static_cast<size_t>(T) * 4);
   l.stage_bytes = (l.plan_base + p.plan_bytes + 15) & ~size_t{15};
   l.total = std::max(l.plan_base + p.total, l.stage_bytes);
   return l;
@@ -1076,7 +1097,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   if (hipGetDevice(&dev) != hipSuccess || dev != g->device)
     return fail(CB_ERR_INVALID_ARG, "cb_graph_step: the graph belongs to device %d, current is %d", g->device, dev);
   const cb_shape* sh = &g->shape;
-  const StepLayout host_l = step_layout(num_reqs, max_blocks_per_req);
+  const StepLayout host_l = step_layout(num_reqs, max_blocks_per_req, num_tokens);
   cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr, host_l);
   int st = check_batch(sh, &b);
   if (st) return st;
@@ -1086,7 +1107,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
     return st;
   Plan p;
   make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0, false);
-  const GraphLayout l = graph_layout(num_reqs, max_blocks_per_req, p);
+  const GraphLayout l = graph_layout(num_reqs, max_blocks_per_req, num_tokens, p);
   const bool fits = g->captured && l.stage_bytes <= g->cap_stage && l.total <= g->ws_bytes &&
                     p.mfma_decode == g->mfma_decode && p.group == g->group && g_tuning.prefill_touch == g->touch;
   if (!fits && (st = graph_capture(g, p, l))) return st;
@@ -1126,10 +1147,14 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   d.off_prefill = static_cast<int64_t>(l.plan_base + p.off_prefill);
   d.off_part_o = static_cast<int64_t>(l.plan_base + p.off_part_o);
   d.off_part_ml = static_cast<int64_t>(l.plan_base + p.off_part_ml);
+  d.off_slots = slots_fit(sh) ? static_cast<int64_t>(l.off_slots) : 0;
   std::memcpy(host, &d, sizeof(d));
   std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
   std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
   std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
+  if (d.off_slots)
+    fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
+               reinterpret_cast<int32_t*>(host + l.off_slots));
   write_plan(p, host + l.plan_base);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipGraphLaunch(sl.exec, s);

@@ -108,6 +108,7 @@ __device__ __forceinline__ void resolve_desc(AppendArgs& a) {
   a.cu_q_lens = desc_array<const int32_t>(d, d->off_cu);
   a.ctx_lens = desc_array<const int32_t>(d, d->off_ctx);
   a.block_tables = desc_array<const int32_t>(d, d->off_bt);
+  a.slots = d->off_slots ? desc_array<const int32_t>(d, d->off_slots) : nullptr;
 }
 
 __device__ __forceinline__ void resolve_desc(RowArgs& a) {

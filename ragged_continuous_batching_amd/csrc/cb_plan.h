@@ -48,6 +48,7 @@ struct StepDesc {
   int32_t n_combine_rows;       // rows merged by the combine pass
   int32_t n_prefill;            // prefill work-groups, empty launch-order slots included
   int64_t off_cu, off_ctx, off_bt, off_splits, off_combine, off_prefill, off_part_o, off_part_ml;
+  int64_t off_slots;            // per-row cache slots (AppendArgs::slots); 0: none
 };
 constexpr int kDescBytes = 256;        // the header's slot at the head of the workspace
 
@@ -66,6 +67,9 @@ struct AppendArgs {
   const int32_t* block_tables;
   int32_t num_reqs, num_tokens, max_blocks, num_kv_heads, num_blocks;
   const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
+  // Optional [num_tokens] cache slot of each packed row (block * block_size + offset), from
+  // the host; null: each row's slot is looked up from cu_q_lens, ctx_lens and the tables.
+  const int32_t* slots;
 };
 
 struct RowArgs {

@@ -8,7 +8,8 @@
 // Layout (include/cb.h): K pages are [block_size][D], V pages are [D][block_size] (V is
 // stored transposed). A work-group takes 16 consecutive packed rows and up to 4 kv heads:
 //   1. every thread loads its 16-byte chunks of the new K and V rows, while the first 16
-//      threads find each row's request, block and slot;
+//      threads find each row's block and slot (from the host's slot list when the step
+//      entry point provides one, else from the request's context length and block table);
 //   2. K chunks go straight to their slots (key rows stay contiguous); V rows are staged in
 //      LDS;
 //   3. V^T leaves LDS per d-row: a group of 16/ES rows that occupies consecutive, aligned
@@ -59,10 +60,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     int blk = -1, off = 0;
     if (tid < nrows) {
       const int t = t0 + tid;
-      const int r = find_request(a.cu_q_lens, a.num_reqs, t);
-      const int p = a.ctx_lens[r] + (t - a.cu_q_lens[r]);
-      blk = a.block_tables[static_cast<int64_t>(r) * a.max_blocks + p / kBlockSize];
-      off = p % kBlockSize;
+      if (a.slots) {                            // the host's slot: one load instead of a chain
+        const int sl = a.slots[t];
+        blk = sl >= 0 ? sl / kBlockSize : -1;
+        off = sl >= 0 ? sl % kBlockSize : 0;
+      } else {
+        const int r = find_request(a.cu_q_lens, a.num_reqs, t);
+        const int p = a.ctx_lens[r] + (t - a.cu_q_lens[r]);
+        blk = a.block_tables[static_cast<int64_t>(r) * a.max_blocks + p / kBlockSize];
+        off = p % kBlockSize;
+      }
       if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = -1;
     }
     info_blk[tid] = blk;
