@@ -148,6 +148,10 @@ def main(argv=None):
                     help="also time the step as a captured HIP graph (cb_graph_step, T-bucketed); value is the "
                          "graph's rate and the roofline kernel durations come from the eager pass of the same run "
                          "(configs 2-4); with --config 5 the whole trace replays through graphs")
+    ap.add_argument("--long-chunk", type=int, default=0, metavar="N",
+                    help="instead of a config: one 256-row prefill chunk after N cached tokens (a late chunk "
+                         "of a long prompt; Hq = Hkv = 32, D = 128, bf16), the case where prefill tiles are "
+                         "split over key ranges")
     ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                     help="cb_set_tuning(KEY, VALUE) before the run (repeatable)")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -187,10 +191,17 @@ def main(argv=None):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    wl = W.config(args.config)
     names = {2: "llama2-7b-shaped mixed step (64 decodes + 2x992 prefill chunks)",
              3: "decode-only GQA (256 decodes, lognormal contexts)",
              4: "chunked-prefill-heavy (4x2048-token chunks)"}
+    if args.long_chunk:
+        n = args.long_chunk
+        wl = W.custom([W.Request(0, n + 256, 1 << 20, cached=n, generated=0)], num_q_heads=32, num_kv_heads=32,
+                      head_dim=128, dtype="bf16", seed=1006, token_budget=256)
+        args.config = 0
+        names[0] = f"late chunk of a long prompt (256 rows after {n} cached tokens, Hq=Hkv=32, D=128)"
+    else:
+        wl = W.config(args.config)
     run = DeviceRun(wl, stale=None)
     base = run.sched
     # setup: write the cached history once (not timed)
@@ -257,7 +268,7 @@ def main(argv=None):
             kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
     cb.cb_profile_reset()
 
-    dominant = "prefill" if args.config == 4 else "decode"
+    dominant = "prefill" if args.config in (0, 4) else "decode"
     if dominant == "decode" and "mixed" in kernels:
         dominant = "mixed"                 # prefill tiles and decode waves in one launch
     avg_s = kernels[dominant]["avg_us"] * 1e-6

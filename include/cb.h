@@ -242,6 +242,11 @@ const char* cb_version(void);
  *   "prefill_waves"  waves per bf16 prefill work-group: 4 (128 query rows, two work-groups
  *                    per CU), 8 (256 rows, one per CU), or 0 (default) = 8 when a step has at
  *                    least 2 x 256 such work-groups, else 4
+ *   "prefill_split"  1 (default): when a bf16 step has fewer prefill work-groups than the
+ *                    GPU has work-group slots, prefill tiles with long key walks are split
+ *                    over key ranges (partials merged by the combine pass); 0: never
+ *   "prefill_split_tiles"  key tiles (64 keys) per split range, forcing splits in any step;
+ *                    0 (default) = automatic
  *   "mixed_launch"   1: a bf16 step with both prefill rows and grouped-query decode rows
  *                    (Hq/Hkv >= 4) runs its prefill tiles (128-row work-groups) and decode
  *                    waves in one launch, interleaved so that both kinds share every CU;

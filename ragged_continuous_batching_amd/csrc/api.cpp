@@ -47,6 +47,10 @@ struct Tuning {
   int32_t prefill_snake = 1;      // 1: alternate rounds of each XCD's prefill queue reversed
   int32_t prefill_waves = 0;      // waves per prefill work-group: 4, 8 (32 query rows each) or
                                   // 0 = 8 when that still gives two work-groups per CU, else 4
+  int32_t prefill_split = 1;      // 1: split the key walk of long prefill tiles when the step
+                                  // has fewer prefill work-groups than slots (partials merged
+                                  // by the combine pass)
+  int32_t prefill_split_tiles = 0;  // key tiles per split, forcing splits (tests); 0 = automatic
   int32_t mixed_launch = 0;       // 1: prefill tiles and matrix-core decode waves in one launch
   int32_t mixed_order = 0;        // 0: merge prefill and decode chunks in proportion to their
                                   // counts; 1: alternate them until one kind runs out
@@ -295,9 +299,11 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
   // rows that take the split-K path, longest first
   struct Row { int32_t token, req, kv_len; };
   struct PrefillGroup { std::vector<PrefillItem> items; int64_t cost = 0; };
+  struct QTile { int32_t req, qb, n_kt, n_split; };      // one row tile of a prefill chunk
   std::vector<PrefillGroup> groups;
+  std::vector<QTile> qtiles;
   std::vector<Row> rows;
-  int64_t total_blocks = 0;
+  int64_t total_blocks = 0, total_tiles = 0;
   for (int32_t r = 0; r < b->num_reqs; ++r) {
     const int32_t t0 = b->h_cu_q_lens[r], q = b->h_cu_q_lens[r + 1] - t0, c = b->h_ctx_lens[r];
     if (q == 0) continue;
@@ -307,22 +313,73 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
         total_blocks += ceil_div(c + i + 1, kBlockSize);
       }
     } else {
-      // one group per (request, kv head): all its q-tiles and query heads read the same
-      // key/value tiles, so they are kept on one XCD (shared L2) and run side by side
       const int32_t rows = 32 * p.prefill_waves;
-      const int32_t n_qt = ceil_div(q, rows);
+      for (int32_t qt = ceil_div(q, rows) - 1; qt >= 0; --qt) {
+        const int32_t qb = qt * rows;
+        qtiles.push_back({r, qb, ceil_div(c + std::min(qb + rows, q), kPrefillKeys), 1});
+        total_tiles += static_cast<int64_t>(qtiles.back().n_kt) * s->num_q_heads;
+      }
+    }
+  }
+  // Split-K for prefill tiles when a step has fewer prefill work-groups than the machine has
+  // work-group slots: a late chunk of a long prompt has few rows but a long context, and its
+  // few work-groups would each walk every key tile while most CUs idle. Tiles longer than
+  // the step's work per slot (at least 16 key tiles) are then cut into near-equal key
+  // ranges, which brings the count of work-groups up to about the slots. With as many
+  // work-groups as slots or more, the CUs already share the work evenly (long and short
+  // work-groups pair up on each CU), and splitting only adds partials: measured on the
+  // Llama-2-7B-shaped mixed step, 512 work-groups, prefill 58 -> 62 us, combine 5 -> 15 us.
+  // Every cut lies at or below the first row's last key ((c + qb) / 64 tiles are fully
+  // visible to every row of the tile), so no row meets an empty range.
+  const int64_t slots = static_cast<int64_t>(kNumCUs) * (p.prefill_waves == 8 ? 1 : 2);
+  const int64_t pre_items = static_cast<int64_t>(qtiles.size()) * s->num_q_heads;
+  if (!qtiles.empty() && g_tuning.prefill_split && (pre_items < slots || g_tuning.prefill_split_tiles > 0)) {
+    const int64_t len = g_tuning.prefill_split_tiles > 0
+                            ? g_tuning.prefill_split_tiles
+                            : std::max<int64_t>(16, (total_tiles + slots - 1) / slots);
+    for (QTile& t : qtiles) {
+      const int32_t c = b->h_ctx_lens[t.req];
+      const int32_t lim = (c + t.qb) / kPrefillKeys;
+      int32_t n = static_cast<int32_t>(std::min<int64_t>((t.n_kt + len - 1) / len, 0xffff));
+      while (n > 1 && static_cast<int64_t>(n - 1) * t.n_kt / n > lim) --n;
+      t.n_split = std::max(n, 1);
+    }
+  }
+  {
+    // one group per (request, kv head): all its q-tiles and query heads read the same
+    // key/value tiles, so they are kept on one XCD (shared L2) and run side by side
+    const int32_t rows = 32 * p.prefill_waves;
+    size_t i0 = 0;
+    while (i0 < qtiles.size()) {
+      size_t i1 = i0;
+      while (i1 < qtiles.size() && qtiles[i1].req == qtiles[i0].req) ++i1;
+      const int32_t r = qtiles[i0].req, t0 = b->h_cu_q_lens[r], q = b->h_cu_q_lens[r + 1] - t0;
+      std::vector<int32_t> part_base(i1 - i0, -1);
+      for (size_t i = i0; i < i1; ++i) {          // partial slots and combine rows of split tiles
+        const QTile& t = qtiles[i];
+        if (t.n_split == 1) continue;
+        part_base[i - i0] = p.n_parts;
+        const int32_t valid = std::min(rows, q - t.qb);
+        for (int32_t k = 0; k < valid; ++k) p.combine.push_back({t0 + t.qb + k, p.n_parts + k * t.n_split, t.n_split, 0});
+        p.n_parts += valid * t.n_split;
+      }
       for (int32_t g = 0; g < s->num_kv_heads; ++g) {
         PrefillGroup grp;
-        for (int32_t qt = n_qt - 1; qt >= 0; --qt) {
-          const int32_t qb = qt * rows;
-          const int32_t tiles = ceil_div(c + std::min(qb + rows, q), kPrefillKeys);
-          for (int32_t hh = 0; hh < q_per_kv; ++hh) {
-            grp.items.push_back({r, qb, g * q_per_kv + hh, tiles});
-            grp.cost += tiles;
+        for (size_t i = i0; i < i1; ++i) {
+          const QTile& t = qtiles[i];
+          for (int32_t sp = 0; sp < t.n_split; ++sp) {
+            const int32_t k0 = static_cast<int32_t>(static_cast<int64_t>(sp) * t.n_kt / t.n_split);
+            const int32_t k1 = static_cast<int32_t>(static_cast<int64_t>(sp + 1) * t.n_kt / t.n_split);
+            for (int32_t hh = 0; hh < q_per_kv; ++hh) {
+              grp.items.push_back({r, t.qb, g * q_per_kv + hh, k1 - k0, k0, k1, part_base[i - i0],
+                                   t.n_split > 1 ? (t.n_split << 16) | sp : 0});
+              grp.cost += k1 - k0;
+            }
           }
         }
         groups.push_back(std::move(grp));
       }
+      i0 = i1;
     }
   }
   // Work-groups are dispatched round-robin over the XCDs (block b runs on XCD b % n). Groups
@@ -351,7 +408,7 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
     }
     size_t depth = 0;
     for (const auto& qx : queue) depth = std::max(depth, qx.size());
-    p.prefill.assign(depth * nx, PrefillItem{-1, 0, 0, 0});
+    p.prefill.assign(depth * nx, PrefillItem{-1, 0, 0, 0, 0, 0, -1, 0});
     for (int x = 0; x < nx; ++x)
       for (size_t k = 0; k < queue[x].size(); ++k) p.prefill[k * nx + x] = queue[x][k];
   }
@@ -442,6 +499,10 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.prefill_waves = value;
   } else if (std::strcmp(key, "prefill_snake") == 0) {
     g_tuning.prefill_snake = value != 0;
+  } else if (std::strcmp(key, "prefill_split") == 0) {
+    g_tuning.prefill_split = value != 0;
+  } else if (std::strcmp(key, "prefill_split_tiles") == 0) {
+    g_tuning.prefill_split_tiles = value;
   } else if (std::strcmp(key, "mixed_launch") == 0) {
     g_tuning.mixed_launch = value != 0;
   } else if (std::strcmp(key, "mixed_order") == 0) {
@@ -583,7 +644,8 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
   const PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
                        batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
                        shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks,
-                       scale_log2, g_tuning.prefill_touch};
+                       scale_log2, g_tuning.prefill_touch, nullptr,
+                       reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml)};
   const RowArgs ra{q, k_cache, v_cache, o,
                    reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml),
                    reinterpret_cast<const RowSplit*>(ws), batch->block_tables,

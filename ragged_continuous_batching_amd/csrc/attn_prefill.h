@@ -75,7 +75,8 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   const bool wave_active = wave_row0 < nq;
   const int wave_keys = c + min(wave_row0 + 31, nq - 1) + 1;  // keys any row of the wave sees
   const int wg_keys = c + min(it.q_begin + ROWS - 1, nq - 1) + 1;
-  const int n_tiles = (wg_keys + kPrefillKeys - 1) / kPrefillKeys;
+  const int kt0 = it.kt_begin;                                // absolute first key tile
+  const int n_tiles = it.kt_end - kt0;                        // tiles of this item (local 0..)
   const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
@@ -185,8 +186,9 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   // One key tile j whose scores are in s_cur: mask, softmax, O += V P. The scores of tile
   // j+1 (other LDS buffer) are computed into s_next in the same straight-line block as the
   // exp2 work of tile j, so the matrix core and the vector ALU overlap within the wave.
-  auto tile_step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
-    const int buf = j & 1;
+  auto tile_step = [&](int u, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    const int buf = u & 1;                       // local index: buffers and register sets
+    const int j = kt0 + u;                       // absolute tile: positions and masks
     if (!wave_active || j * kPrefillKeys >= wave_keys) return;
     const bool diag = __builtin_amdgcn_readfirstlane(j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0);
     if (diag) {                                  // causal mask, only on tiles crossing it
@@ -271,16 +273,16 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
 
   // prologue: tiles 0 and 1 in LDS, the scores of tile 0 computed, the next NSET tiles in
   // flight (tile t is staged in register set t % NSET)
-  load_tile(0, 0);
+  load_tile(kt0, 0);
   store_tile(0, 0);
-  if (n_tiles > 1) load_tile(1, 1 % NSET);
+  if (n_tiles > 1) load_tile(kt0 + 1, 1 % NSET);
   __syncthreads();
   f32x16 sa[2], sb[2];
   if (wave_active) compute_s(0, sa);
   if (n_tiles > 1) {
     store_tile(1, 1 % NSET);
-    if (n_tiles > 2) load_tile(2, 0);
-    if (NSET == 2 && n_tiles > 3) load_tile(3, 1 % NSET);
+    if (n_tiles > 2) load_tile(kt0 + 2, 0);
+    if (NSET == 2 && n_tiles > 3) load_tile(kt0 + 3, 1 % NSET);
   }
   __syncthreads();
   // Per tile j: step (reads buffer j&1, scores of j+1 from the other buffer), a barrier
@@ -292,7 +294,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     __syncthreads();
     if (j + 2 < n_tiles) {
       store_tile(j & 1, j % NSET);
-      if (j + 2 + NSET < n_tiles) load_tile(j + 2 + NSET, j % NSET);
+      if (j + 2 + NSET < n_tiles) load_tile(kt0 + j + 2 + NSET, j % NSET);
     }
     __syncthreads();
   };
@@ -309,6 +311,23 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
   if (qrow >= nq) return;
+  if (it.part_base >= 0) {                     // one split of the key range: partials
+    const int n_split = it.split >> 16;
+    const int64_t part = it.part_base + static_cast<int64_t>(qrow - it.q_begin) * n_split + (it.split & 0xffff);
+    float* po = a.part_o + (part * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(po + dt * 32 + q4 * 8 + grp * 4) =
+            f32x4{oacc[dt][q4 * 4 + 0], oacc[dt][q4 * 4 + 1], oacc[dt][q4 * 4 + 2], oacc[dt][q4 * 4 + 3]};
+    if (grp == 0) {
+      float* ml = a.part_ml + (part * a.num_q_heads + h) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+    return;
+  }
   const float inv = 1.f / l_tot;
   uint16_t* op = static_cast<uint16_t*>(a.o) + (static_cast<int64_t>(t0 + qrow) * a.num_q_heads + h) * D;
 #pragma unroll

@@ -137,6 +137,8 @@ __device__ __forceinline__ void resolve_desc(PrefillArgs& a) {
   a.cu_q_lens = desc_array<const int32_t>(d, d->off_cu);
   a.ctx_lens = desc_array<const int32_t>(d, d->off_ctx);
   a.block_tables = desc_array<const int32_t>(d, d->off_bt);
+  a.part_o = desc_array<float>(d, d->off_part_o);
+  a.part_ml = desc_array<float>(d, d->off_part_ml);
 }
 
 }  // namespace cb

@@ -28,12 +28,22 @@ struct CombineRow {
 };
 
 // One tile of a prefill chunk: rows q_begin .. q_begin+R-1 of request `req` (R = 32 x the
-// work-group's waves, clipped to its row count), query head `head`. req < 0 marks an empty slot.
+// work-group's waves, clipped to its row count), query head `head`, key tiles
+// kt_begin .. kt_end-1 (64 keys each). req < 0 marks an empty slot. part_base < 0: the item
+// walks all of its rows' keys and writes O. Otherwise it is split `split & 0xffff` of
+// `split >> 16` over the key range: row i of the tile writes its unnormalised output and
+// (max, sum) to partial slot part_base + i * (split >> 16) + (split & 0xffff), and the combine
+// pass merges them. Every split boundary lies at or below the first row's last key, so each
+// row sees at least one key of every split.
 struct PrefillItem {
   int32_t req;
   int32_t q_begin;
   int32_t head;
-  int32_t kv_tiles;     // key tiles this item walks (used for ordering; kept for tracing)
+  int32_t kv_tiles;     // key tiles this item walks (its cost in the launch order)
+  int32_t kt_begin;
+  int32_t kt_end;
+  int32_t part_base;
+  int32_t split;
 };
 
 // Header at the start of a captured step's workspace (cb_graph_*). The host writes it into
@@ -112,6 +122,8 @@ struct PrefillArgs {
   float scale_log2;
   int32_t touch_ahead;    // 1: pull the key tile two steps ahead toward L2
   const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
+  float* part_o;          // partial outputs of split items, as RowArgs::part_o / part_ml
+  float* part_ml;
 };
 
 // One launch holding a step's prefill tiles and its matrix-core decode waves (4-wave

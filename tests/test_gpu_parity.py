@@ -574,3 +574,37 @@ def test_mixed_launch_trace_replay():
     finally:
         cb.cb_set_tuning("mixed_launch", 0)
     assert checked == 5
+
+
+# --------------------------------------------------------------------------------------
+# split-K of long prefill tiles ("prefill_split"); partials merged by the combine pass
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,hq,hkv,d,waves,split_tiles,mixed", [
+    ("mixed", 8, 2, 128, 4, 2, 0), ("tile_edges", 4, 4, 128, 4, 1, 0), ("mixed", 4, 2, 64, 4, 3, 0),
+    ("tile_edges", 8, 2, 128, 8, 2, 0), ("mixed", 16, 2, 128, 4, 2, 1), ("long_decode", 16, 4, 128, 4, 5, 0)])
+def test_prefill_split_against_oracle(name, hq, hkv, d, waves, split_tiles, mixed):
+    """Tiny split lengths force several key ranges per prefill tile (cuts at or below each
+    tile's first row), with 4- and 8-wave work-groups and in the mixed launch."""
+    wl = small_workload(name, hq, hkv, d, "bf16")
+    try:
+        cb.cb_set_tuning("prefill_split_tiles", split_tiles)
+        cb.cb_set_tuning("prefill_waves", waves)
+        cb.cb_set_tuning("mixed_launch", mixed)
+        run, step, batch, o = run_one_step(wl)
+    finally:
+        cb.cb_set_tuning("prefill_split_tiles", 0)
+        cb.cb_set_tuning("prefill_waves", 0)
+        cb.cb_set_tuning("mixed_launch", 0)
+    check(o, oracle_full(wl, step), "bf16", f"prefill split {split_tiles} {name} Hq={hq} Hkv={hkv} D={d} w={waves}")
+
+
+def test_prefill_split_off_matches_oracle_config2():
+    """Config 2 with prefill splitting off (the default splits its c = 1024 chunk)."""
+    wl = W.config(2, value_reading="unit")
+    try:
+        cb.cb_set_tuning("prefill_split", 0)
+        run, step, batch, o = run_one_step(wl)
+    finally:
+        cb.cb_set_tuning("prefill_split", 1)
+    rows, ref = oracle_rows(wl, step, [t for t in sample_rows(step, 24, np.random.default_rng(21)) if t >= 64])
+    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 2 prefill unsplit")
