@@ -123,8 +123,11 @@ int g_ring_next = 0;
 // grown to size (capacities are powers of two). A slot is reused only after its previous
 // copy has completed (event wait). With the stage kernel the copy moves `bytes` rounded up to
 // 16, so `dst` must have room for that.
-template <class Fill>
-int upload(void* dst, size_t bytes, hipStream_t stream, Fill&& fill) {
+//
+// upload_with() leaves the device side to `launch(src_dev, src_host, bytes)`, which must
+// enqueue on `stream` whatever reads the slot (the event after it guards the slot's reuse).
+template <class Fill, class Launch>
+int upload_with(size_t bytes, hipStream_t stream, Fill&& fill, Launch&& launch) {
   if (bytes == 0) return CB_OK;
   bytes = (bytes + 15) & ~static_cast<size_t>(15);
   std::lock_guard<std::mutex> lk(g_ring_mu);
@@ -153,12 +156,19 @@ int upload(void* dst, size_t bytes, hipStream_t stream, Fill&& fill) {
     s.cap = cap;
   }
   fill(static_cast<char*>(s.host));
-  hipError_t e = g_tuning.stage_kernel ? launch_stage_copy(s.host_dev, dst, bytes, stream)
-                                       : hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  hipError_t e = launch(static_cast<const void*>(s.host_dev), static_cast<const void*>(s.host), bytes);
   if (e != hipSuccess) return fail(CB_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
   if (hipEventRecord(s.ev, stream) != hipSuccess) return fail(CB_ERR_HIP, "plan upload: event record failed");
   s.in_flight = true;
   return CB_OK;
+}
+
+template <class Fill>
+int upload(void* dst, size_t bytes, hipStream_t stream, Fill&& fill) {
+  return upload_with(bytes, stream, fill, [&](const void* src_dev, const void* src_host, size_t n) {
+    return g_tuning.stage_kernel ? launch_stage_copy(src_dev, dst, n, stream)
+                                 : hipMemcpyAsync(dst, src_host, n, hipMemcpyHostToDevice, stream);
+  });
 }
 
 // ---- side stream for running prefill tiles beside the decode rows ----------------------
@@ -229,6 +239,8 @@ int check_batch(const cb_shape* s, const cb_batch* b) {
                   ceil_div(static_cast<int64_t>(c) + q, s->block_size), b->max_blocks_per_req);
     if (static_cast<int64_t>(c) + q > (int64_t{1} << 30)) return fail(CB_ERR_INVALID_ARG, "request %d too long", r);
   }
+  if (static_cast<int64_t>(b->num_reqs) * b->max_blocks_per_req > INT32_MAX)
+    return fail(CB_ERR_INVALID_ARG, "block table of %d x %d entries is too large", b->num_reqs, b->max_blocks_per_req);
   if (b->h_cu_q_lens[b->num_reqs] != b->num_tokens)
     return fail(CB_ERR_INVALID_ARG, "cu_q_lens[num_reqs] = %d but num_tokens = %d", b->h_cu_q_lens[b->num_reqs],
                 b->num_tokens);
@@ -270,7 +282,13 @@ bool wants_mixed(const cb_shape* s, const cb_batch* b) {
 
 // force_waves (4 or 8) fixes the prefill work-group size; 0 takes the tuning / automatic choice.
 // allow_mixed = false keeps prefill and decode in separate launches (captured steps).
-void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 0, bool allow_mixed = true) {
+// bt_rows (host, [num_reqs], nullable): where each request's block ids start in the device
+// block table; null means the padded [num_reqs, max_blocks_per_req] layout of cb_batch.
+void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 0, bool allow_mixed = true,
+               const int32_t* bt_rows = nullptr) {
+  auto bt_row = [&](int32_t r) {
+    return bt_rows ? bt_rows[r] : static_cast<int32_t>(static_cast<int64_t>(r) * b->max_blocks_per_req);
+  };
   const int q_per_kv = s->num_q_heads / s->num_kv_heads;
   // query heads per decode wave: all heads of the group up to decode_group; a larger group
   // is covered by n_sub waves on adjacent slots, which read the same pages back to back
@@ -371,7 +389,7 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
             const int32_t k0 = static_cast<int32_t>(static_cast<int64_t>(sp) * t.n_kt / t.n_split);
             const int32_t k1 = static_cast<int32_t>(static_cast<int64_t>(sp + 1) * t.n_kt / t.n_split);
             for (int32_t hh = 0; hh < q_per_kv; ++hh) {
-              grp.items.push_back({r, t.qb, g * q_per_kv + hh, k1 - k0, k0, k1, part_base[i - i0],
+              grp.items.push_back({r, t.qb, g * q_per_kv + hh, bt_row(r), k0, k1, part_base[i - i0],
                                    t.n_split > 1 ? (t.n_split << 16) | sp : 0});
               grp.cost += k1 - k0;
             }
@@ -428,12 +446,13 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
     const int32_t nb = ceil_div(row.kv_len, kBlockSize);
     const int32_t ns = ceil_div(nb, split);
     if (ns == 1) {
-      p.splits.push_back({row.token, row.req, 0, nb, row.kv_len, -1});
+      p.splits.push_back({row.token, bt_row(row.req), 0, nb, row.kv_len, -1});
       continue;
     }
     p.combine.push_back({row.token, p.n_parts, ns, 0});
     for (int32_t k = 0; k < ns; ++k)
-      p.splits.push_back({row.token, row.req, k * split, std::min(nb, (k + 1) * split), row.kv_len, p.n_parts + k});
+      p.splits.push_back({row.token, bt_row(row.req), k * split, std::min(nb, (k + 1) * split), row.kv_len,
+                          p.n_parts + k});
     p.n_parts += ns;
   }
 
@@ -707,12 +726,13 @@ struct StepLayout {
   size_t off_cu = 0, off_ctx = 0, off_bt = 0, off_slots = 0, meta_bytes = 0, plan_base = 0;
 };
 
-StepLayout step_layout(int32_t R, int32_t maxb, int32_t T) {
+// bt_entries: block-table entries staged (the compact table's length, or R * max_blocks).
+StepLayout step_layout(int32_t R, int64_t bt_entries, int32_t T) {
   StepLayout l;
   l.off_cu = 0;
   l.off_ctx = static_cast<size_t>(R + 1) * 4;
   l.off_bt = l.off_ctx + static_cast<size_t>(R) * 4;
-  l.off_slots = l.off_bt + static_cast<size_t>(R) * maxb * 4;
+  l.off_slots = l.off_bt + static_cast<size_t>(bt_entries) * 4;
   l.meta_bytes = l.off_slots + static_cast<size_t>(std::max(T, 0)) * 4;
   l.plan_base = align256(l.meta_bytes);
   return l;
@@ -731,6 +751,31 @@ void fill_slots(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, 
 // Slots fit an int32 for every pool this library accepts in practice; larger pools keep the
 // device-side lookup.
 inline bool slots_fit(const cb_shape* s) { return s->num_blocks <= INT32_MAX / kBlockSize; }
+
+// The step entry points stage a compact block table: request r's ceil((c + q) / bs) ids (none
+// for a request with no rows) start at rows[r]. The padded [R, max_blocks] table of a long
+// request beside many short ones is mostly padding (the decode-only workload: 2.1 MB staged
+// per step, 0.2 MB of it block ids). Returns the entry count.
+int64_t compact_rows(int32_t R, const int32_t* cu, const int32_t* ctx, std::vector<int32_t>& rows) {
+  rows.resize(static_cast<size_t>(R));
+  int64_t n = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    rows[r] = static_cast<int32_t>(n);
+    const int32_t q = cu[r + 1] - cu[r];
+    if (q > 0) n += ceil_div(static_cast<int64_t>(ctx[r]) + q, kBlockSize);
+  }
+  return n;
+}
+
+void fill_compact(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt,
+                  const std::vector<int32_t>& rows, int32_t* out) {
+  for (int32_t r = 0; r < R; ++r) {
+    const int32_t q = cu[r + 1] - cu[r];
+    if (q > 0)
+      std::memcpy(out + rows[r], bt + static_cast<size_t>(r) * maxb,
+                  static_cast<size_t>(ceil_div(static_cast<int64_t>(ctx[r]) + q, kBlockSize)) * 4);
+  }
+}
 
 }  // namespace
 }  // namespace cb
@@ -786,11 +831,16 @@ extern "C" size_t cb_step_workspace_size(const cb_shape* shape, int32_t num_reqs
                                          int32_t max_blocks_per_req, const int32_t* h_cu_q_lens,
                                          const int32_t* h_ctx_lens) {
   if (check_shape(shape) || num_reqs < 0 || max_blocks_per_req < 0) return 0;
-  const StepLayout l = step_layout(num_reqs, max_blocks_per_req, num_tokens);
-  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr, l);
+  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr,
+                          step_layout(num_reqs, 0, num_tokens));
   if (check_batch(shape, &b) || num_tokens == 0) return 0;
+  std::vector<int32_t> rows;
+  const bool compact = slots_fit(shape);
+  const int64_t nbt = compact ? compact_rows(num_reqs, h_cu_q_lens, h_ctx_lens, rows)
+                              : static_cast<int64_t>(num_reqs) * max_blocks_per_req;
+  const StepLayout l = step_layout(num_reqs, nbt, num_tokens);
   Plan p;
-  make_plan(shape, &b, p);
+  make_plan(shape, &b, p, 0, true, compact ? rows.data() : nullptr);
   return l.plan_base + p.total;
 }
 
@@ -801,11 +851,19 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   int st = check_shape(shape);
   if (st) return st;
   if (num_reqs < 0 || max_blocks_per_req < 0) return fail(CB_ERR_INVALID_ARG, "cb_step_forward: negative count");
-  const StepLayout l = step_layout(num_reqs, max_blocks_per_req, num_tokens);
   char* ws = static_cast<char*>(workspace);
-  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, ws, l);
+  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr,
+                          step_layout(num_reqs, 0, num_tokens));
   if ((st = check_batch(shape, &b))) return st;
   if (num_tokens == 0) return CB_OK;
+  // slots and the compact block table go together: with them, no kernel indexes the table
+  // by max_blocks_per_req (the append takes slots, the rest take each item's bt_row)
+  const bool slots = slots_fit(shape);
+  std::vector<int32_t> bt_rows;
+  const int64_t nbt = slots ? compact_rows(num_reqs, h_cu_q_lens, h_ctx_lens, bt_rows)
+                            : static_cast<int64_t>(num_reqs) * max_blocks_per_req;
+  const StepLayout l = step_layout(num_reqs, nbt, num_tokens);
+  b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, ws, l);
   if ((st = check_block_ids(shape, num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
                              "cb_step_forward")))
     return st;
@@ -813,7 +871,7 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
     return fail(CB_ERR_INVALID_ARG, "cb_step_forward: new K/V must be non-NULL and 16-byte aligned");
   if ((st = check_tensors(q, k_cache, v_cache, o, scale, "cb_step_forward"))) return st;
   Plan p;
-  make_plan(shape, &b, p);
+  make_plan(shape, &b, p, 0, true, slots ? bt_rows.data() : nullptr);
   if (!ws || workspace_bytes < l.plan_base + p.total)
     return fail(CB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes,
                 l.plan_base + p.total);
@@ -821,24 +879,40 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
 
   // one upload: metadata, then the plan
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = upload(ws, l.plan_base + p.plan_bytes, s, [&](char* host) {
+  auto fill = [&](char* host) {
     std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
     std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
-    std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
-    if (slots_fit(shape))
+    if (slots) {
+      fill_compact(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, bt_rows,
+                   reinterpret_cast<int32_t*>(host + l.off_bt));
       fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
                  reinterpret_cast<int32_t*>(host + l.off_slots));
+    } else {
+      std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
+    }
     write_plan(p, host + l.plan_base);
-  });
-  if (st) return st;
-
+  };
   AppendArgs aa{k_new, v_new, k_cache, v_cache, b.cu_q_lens, b.ctx_lens, b.block_tables, num_reqs, num_tokens,
                 max_blocks_per_req, shape->num_kv_heads, shape->num_blocks, nullptr,
-                slots_fit(shape) ? reinterpret_cast<const int32_t*>(ws + l.off_slots) : nullptr};
-  hipError_t e;
-  {
+                slots ? reinterpret_cast<const int32_t*>(ws + l.off_slots) : nullptr, nullptr, nullptr, 0};
+  const int eb = elem_bytes(shape);
+  hipError_t e = hipSuccess;
+  if (g_tuning.stage_kernel && slots) {
+    // The append launch also moves the staged bytes into the workspace, and takes its slots
+    // straight from the pinned buffer: one kernel fewer per step.
+    st = upload_with(l.plan_base + p.plan_bytes, s, fill, [&](const void* src_dev, const void*, size_t n) {
+      aa.slots = reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + l.off_slots);
+      aa.stage_src = src_dev;
+      aa.stage_dst = ws;
+      aa.stage_n16 = static_cast<int64_t>(n / 16);
+      ProfScope prof(CB_KERNEL_APPEND, s);
+      return e = launch_kv_append(aa, eb, shape->head_dim, s);
+    });
+    if (st) return st;
+  } else {
+    if ((st = upload(ws, l.plan_base + p.plan_bytes, s, fill))) return st;
     ProfScope prof(CB_KERNEL_APPEND, s);
-    e = launch_kv_append(aa, elem_bytes(shape), shape->head_dim, s);
+    e = launch_kv_append(aa, eb, shape->head_dim, s);
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_step_forward: append launch failed: %s", hipGetErrorString(e));
   return launch_attention(shape, &b, p, ws + l.plan_base, q, k_cache, v_cache, scale, o, s);
@@ -957,12 +1031,12 @@ struct GraphLayout {
   size_t off_cu = 0, off_ctx = 0, off_bt = 0, off_slots = 0, plan_base = 0, stage_bytes = 0, total = 0;
 };
 
-GraphLayout graph_layout(int32_t R, int32_t maxb, int32_t T, const Plan& p) {
+GraphLayout graph_layout(int32_t R, int64_t bt_entries, int32_t T, const Plan& p) {
   GraphLayout l;
   l.off_cu = kDescBytes;
   l.off_ctx = l.off_cu + static_cast<size_t>(R + 1) * 4;
   l.off_bt = l.off_ctx + static_cast<size_t>(R) * 4;
-  l.off_slots = l.off_bt + static_cast<size_t>(R) * maxb * 4;
+  l.off_slots = l.off_bt + static_cast<size_t>(bt_entries) * 4;
   l.plan_base = align256(l.off_slots + static_cast<size_t>(T) * 4);
   l.stage_bytes = (l.plan_base + p.plan_bytes + 15) & ~size_t{15};
   l.total = std::max(l.plan_base + p.total, l.stage_bytes);
@@ -1159,7 +1233,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   if (hipGetDevice(&dev) != hipSuccess || dev != g->device)
     return fail(CB_ERR_INVALID_ARG, "cb_graph_step: the graph belongs to device %d, current is %d", g->device, dev);
   const cb_shape* sh = &g->shape;
-  const StepLayout host_l = step_layout(num_reqs, max_blocks_per_req, num_tokens);
+  const StepLayout host_l = step_layout(num_reqs, 0, num_tokens);
   cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr, host_l);
   int st = check_batch(sh, &b);
   if (st) return st;
@@ -1167,9 +1241,13 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   if ((st = check_block_ids(sh, num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
                             "cb_graph_step")))
     return st;
+  const bool slots = slots_fit(sh);           // with slots, the compact block table (as cb_step_forward)
+  std::vector<int32_t> bt_rows;
+  const int64_t nbt = slots ? compact_rows(num_reqs, h_cu_q_lens, h_ctx_lens, bt_rows)
+                            : static_cast<int64_t>(num_reqs) * max_blocks_per_req;
   Plan p;
-  make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0, false);
-  const GraphLayout l = graph_layout(num_reqs, max_blocks_per_req, num_tokens, p);
+  make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0, false, slots ? bt_rows.data() : nullptr);
+  const GraphLayout l = graph_layout(num_reqs, nbt, num_tokens, p);
   const bool fits = g->captured && l.stage_bytes <= g->cap_stage && l.total <= g->ws_bytes &&
                     p.mfma_decode == g->mfma_decode && p.group == g->group && g_tuning.prefill_touch == g->touch;
   if (!fits && (st = graph_capture(g, p, l))) return st;
@@ -1209,14 +1287,18 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   d.off_prefill = static_cast<int64_t>(l.plan_base + p.off_prefill);
   d.off_part_o = static_cast<int64_t>(l.plan_base + p.off_part_o);
   d.off_part_ml = static_cast<int64_t>(l.plan_base + p.off_part_ml);
-  d.off_slots = slots_fit(sh) ? static_cast<int64_t>(l.off_slots) : 0;
+  d.off_slots = slots ? static_cast<int64_t>(l.off_slots) : 0;
   std::memcpy(host, &d, sizeof(d));
   std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
   std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
-  std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
-  if (d.off_slots)
+  if (slots) {
+    fill_compact(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, bt_rows,
+                 reinterpret_cast<int32_t*>(host + l.off_bt));
     fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
                reinterpret_cast<int32_t*>(host + l.off_slots));
+  } else {
+    std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
+  }
   write_plan(p, host + l.plan_base);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipGraphLaunch(sl.exec, s);

@@ -65,7 +65,7 @@ __device__ __forceinline__ void row_attn_mfma_waves(RowArgs a, int wg) {
   for (int t = 0; t < DT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(sp.req) * a.max_blocks;
+  const int32_t* bt = a.block_tables + sp.bt_row;
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);

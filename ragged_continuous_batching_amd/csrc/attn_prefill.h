@@ -77,7 +77,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   const int wg_keys = c + min(it.q_begin + ROWS - 1, nq - 1) + 1;
   const int kt0 = it.kt_begin;                                // absolute first key tile
   const int n_tiles = it.kt_end - kt0;                        // tiles of this item (local 0..)
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(r) * a.max_blocks;
+  const int32_t* bt = a.block_tables + it.bt_row;
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
     for (int i = 0; i < NLV; ++i) acc[j][i] = 0.f;
   }
 
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(sp.req) * a.max_blocks;
+  const int32_t* bt = a.block_tables + sp.bt_row;
   const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);

@@ -7,12 +7,13 @@
 namespace cb {
 
 // One split of one single-row attention (a decode row, or any row of an fp32 prefill):
-// keys [blk_begin*bs, min(blk_end*bs, kv_len)) of request `req`, for packed row `token`.
-// part < 0: the row has one split and the kernel writes O directly; otherwise the split's
-// unnormalised output and (max, sum) go to partial slot `part` and a combine pass merges.
+// keys [blk_begin*bs, min(blk_end*bs, kv_len)) of the row's request, for packed row `token`;
+// the request's block ids start at block_tables[bt_row]. part < 0: the row has one split
+// and the kernel writes O directly; otherwise the split's unnormalised output and
+// (max, sum) go to partial slot `part` and a combine pass merges.
 struct RowSplit {
   int32_t token;
-  int32_t req;
+  int32_t bt_row;
   int32_t blk_begin;
   int32_t blk_end;
   int32_t kv_len;
@@ -39,7 +40,7 @@ struct PrefillItem {
   int32_t req;
   int32_t q_begin;
   int32_t head;
-  int32_t kv_tiles;     // key tiles this item walks (its cost in the launch order)
+  int32_t bt_row;       // the request's block ids start at block_tables[bt_row]
   int32_t kt_begin;
   int32_t kt_end;
   int32_t part_base;
@@ -80,6 +81,11 @@ struct AppendArgs {
   // Optional [num_tokens] cache slot of each packed row (block * block_size + offset), from
   // the host; null: each row's slot is looked up from cu_q_lens, ctx_lens and the tables.
   const int32_t* slots;
+  // Optional staging copy done by the same launch: stage_n16 16-byte chunks from stage_src
+  // (the pinned host buffer) to stage_dst (the workspace), for the kernels that follow.
+  const void* stage_src;
+  void* stage_dst;
+  int64_t stage_n16;
 };
 
 struct RowArgs {

@@ -10,6 +10,8 @@
 //   1. every thread loads its 16-byte chunks of the new K and V rows, while the first 16
 //      threads find each row's block and slot (from the host's slot list when the step
 //      entry point provides one, else from the request's context length and block table);
+//      called from the step entry point, the launch also copies the step's staged
+//      metadata and plan into the workspace (no separate copy kernel);
 //   2. K chunks go straight to their slots (key rows stay contiguous); V rows are staged in
 //      LDS;
 //   3. V^T leaves LDS per d-row: a group of 16/ES rows that occupies consecutive, aligned
@@ -55,6 +57,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
       vv[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_new) + src);
       kv[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k_new) + src);
     }
+  }
+  if (a.stage_src) {
+    // The step's metadata and plan, from the pinned staging buffer into the workspace (the
+    // kernels after this one read them there): spread over all work-groups, issued while the
+    // new K/V rows above are in flight.
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * gridDim.y * 256;
+    const u32x4* src = static_cast<const u32x4*>(a.stage_src);
+    u32x4* dst = static_cast<u32x4*>(a.stage_dst);
+    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + tid; i < a.stage_n16;
+         i += stride)
+      dst[i] = src[i];
   }
   if (tid < ROWS) {
     int blk = -1, off = 0;
