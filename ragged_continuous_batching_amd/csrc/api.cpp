@@ -1109,6 +1109,7 @@ int graph_capture(cb_graph* g, const Plan& p, const GraphLayout& l) {
   const cb_shape* sh = &g->shape;
   const int eb = elem_bytes(sh);
   const bool prefill = sh->dtype == CB_BF16;          // fp32 prefill rows take the split-K path
+  const bool fused = slots_fit(sh);                   // staging copy inside the append node
   const float scale_log2 = static_cast<float>(static_cast<double>(g->scale) * kLog2e);
   const StepDesc* desc = static_cast<const StepDesc*>(g->ws);
   for (auto& sl : g->slot) {
@@ -1127,13 +1128,22 @@ int graph_capture(cb_graph* g, const Plan& p, const GraphLayout& l) {
     hipStream_t cs = g->cap_stream;
     if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess)
       return fail(CB_ERR_HIP, "cb_graph_step: hipStreamBeginCapture failed");
-    // the copy's bound (an argument) is the capacity; its grid is set per replay
-    hipError_t e = launch_stage_copy_desc(sl.host_dev, g->ws, g->cap_stage, cs);
-    if (e == hipSuccess) {
-      AppendArgs aa{g->k_new, g->v_new, g->k_cache, g->v_cache, nullptr, nullptr, nullptr, 0, 1, 0,
-                    sh->num_kv_heads, sh->num_blocks, desc};
-      e = launch_kv_append(aa, eb, sh->head_dim, cs);
+    // With per-row slots (any pool up to 2^31 / 16 blocks) the append node also moves the
+    // staged bytes: it reads the header and its slots from the pinned buffer and copies the
+    // rest into the workspace, as cb_step_forward's append does. Otherwise a copy node
+    // (bound: the capacity, an argument; grid set per replay) precedes it.
+    hipError_t e = hipSuccess;
+    AppendArgs aa{g->k_new, g->v_new, g->k_cache, g->v_cache, nullptr, nullptr, nullptr, 0, 1, 0,
+                  sh->num_kv_heads, sh->num_blocks, desc};
+    if (fused) {
+      aa.desc = static_cast<const StepDesc*>(sl.host_dev);
+      aa.stage_src = sl.host_dev;
+      aa.stage_dst = g->ws;
+      aa.stage_n16 = -static_cast<int64_t>(g->cap_stage / 16);
+    } else {
+      e = launch_stage_copy_desc(sl.host_dev, g->ws, g->cap_stage, cs);
     }
+    if (e == hipSuccess) e = launch_kv_append(aa, eb, sh->head_dim, cs);
     if (e == hipSuccess && prefill) {
       PrefillArgs pa{g->q, g->k_cache, g->v_cache, g->o, nullptr, nullptr, nullptr, nullptr, 1,
                      sh->num_q_heads, sh->num_kv_heads, 0, sh->num_blocks, scale_log2, g->touch, desc};
@@ -1157,7 +1167,7 @@ int graph_capture(cb_graph* g, const Plan& p, const GraphLayout& l) {
     const int kinds[] = {kNodeStage, kNodeAppend, kNodePrefill, kNodeDecode, kNodeCombine};
     std::vector<int> order;
     for (int k : kinds)
-      if (k != kNodePrefill || prefill) order.push_back(k);
+      if ((k != kNodePrefill || prefill) && (k != kNodeStage || !fused)) order.push_back(k);
     if (chain.size() != order.size())
       return fail(CB_ERR_HIP, "cb_graph_step: captured %zu kernels, expected %zu", chain.size(), order.size());
     for (size_t i = 0; i < chain.size(); ++i) {

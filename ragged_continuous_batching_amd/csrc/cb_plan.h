@@ -83,6 +83,8 @@ struct AppendArgs {
   const int32_t* slots;
   // Optional staging copy done by the same launch: stage_n16 16-byte chunks from stage_src
   // (the pinned host buffer) to stage_dst (the workspace), for the kernels that follow.
+  // stage_n16 < 0 (a replayed step): the count is the header's stage_bytes / 16, at most
+  // -stage_n16.
   const void* stage_src;
   void* stage_dst;
   int64_t stage_n16;

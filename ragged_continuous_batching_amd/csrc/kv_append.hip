@@ -63,10 +63,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     // kernels after this one read them there): spread over all work-groups, issued while the
     // new K/V rows above are in flight.
     const int64_t stride = static_cast<int64_t>(gridDim.x) * gridDim.y * 256;
+    const int64_t n16 = a.stage_n16 >= 0 ? a.stage_n16 : min(a.desc->stage_bytes / 16, -a.stage_n16);
     const u32x4* src = static_cast<const u32x4*>(a.stage_src);
     u32x4* dst = static_cast<u32x4*>(a.stage_dst);
-    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + tid; i < a.stage_n16;
-         i += stride)
+    for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + tid; i < n16; i += stride)
       dst[i] = src[i];
   }
   if (tid < ROWS) {
