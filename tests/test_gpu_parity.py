@@ -608,3 +608,52 @@ def test_prefill_split_off_matches_oracle_config2():
         cb.cb_set_tuning("prefill_split", 1)
     rows, ref = oracle_rows(wl, step, [t for t in sample_rows(step, 24, np.random.default_rng(21)) if t >= 64])
     check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 2 prefill unsplit")
+
+
+def test_requests_with_no_rows_in_every_entry_point():
+    """A request may take no rows in a step (q = 0 is legal). Its block ids are not staged
+    (compact tables) and it gets no slots; every entry point must skip it, and all other
+    rows match the two-call form bit for bit and the oracle."""
+    wl = small_workload("mixed", 8, 2, 128, "bf16")
+    run = DeviceRun(wl)
+    step = run.sched.build()
+    run.write_history(step)
+    q, k, v = run.step_inputs(step)
+    # insert empty requests before, between and after the real ones (same tables)
+    R = step.num_reqs
+    order = [None]
+    for i in range(R):
+        order += [i, None]
+    cu, ctx, rows = [0], [], []
+    for x in order:
+        if x is None:
+            ctx.append(5)
+            rows.append(step.block_tables[0])
+            cu.append(cu[-1])
+        else:
+            n = int(step.cu_q_lens[x + 1] - step.cu_q_lens[x])
+            ctx.append(int(step.ctx_lens[x]))
+            rows.append(step.block_tables[x])
+            cu.append(cu[-1] + n)
+    cu, ctx, bt = np.array(cu, np.int32), np.array(ctx, np.int32), np.stack(rows).astype(np.int32)
+    assert cu[-1] == step.num_tokens
+    shape, T, Rz, maxb = run.shape, step.num_tokens, len(ctx), bt.shape[1]
+    # two-call form with the original batch (reference bits): append, then attend
+    batch = cb.Batch.from_step(step, device=run.device)
+    run.append(batch, k, v)
+    o_ref = run.attention(batch, q)
+    need = cb.cb_step_workspace_size(shape, Rz, T, maxb, cu, ctx)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o1 = torch.empty_like(q)
+    cb.cb_step_forward(shape, Rz, T, maxb, cu, ctx, bt, q, k, v, run.k_cache, run.v_cache, wl.scale, o1, ws, need,
+                       run.stream)
+    o2 = torch.full_like(q, float("nan"))
+    g = cb.cb_graph_create(shape, T, q, k, v, run.k_cache, run.v_cache, wl.scale, o2)
+    try:
+        cb.cb_graph_step(g, Rz, T, maxb, cu, ctx, bt, run.stream)
+        torch.cuda.synchronize()
+    finally:
+        cb.cb_graph_destroy(g)
+    assert torch.equal(o1, o_ref)
+    assert torch.equal(o2, o_ref)
+    check(o1, oracle_full(wl, step), "bf16", "empty requests")
