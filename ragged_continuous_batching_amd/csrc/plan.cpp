@@ -239,10 +239,12 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves, b
       p.splits.push_back({row.token, bt_row(row.req), 0, nb, row.kv_len, -1});
       continue;
     }
+    // near-equal splits (a 209-block row at split 64: 53/52/52/52, not 64/64/64/17), so no
+    // wave pays a full start-up for a sliver of a row
     p.combine.push_back({row.token, p.n_parts, ns, 0});
     for (int32_t k = 0; k < ns; ++k)
-      p.splits.push_back({row.token, bt_row(row.req), k * split, std::min(nb, (k + 1) * split), row.kv_len,
-                          p.n_parts + k});
+      p.splits.push_back({row.token, bt_row(row.req), static_cast<int32_t>(static_cast<int64_t>(k) * nb / ns),
+                          static_cast<int32_t>(static_cast<int64_t>(k + 1) * nb / ns), row.kv_len, p.n_parts + k});
     p.n_parts += ns;
   }
 
