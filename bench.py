@@ -60,9 +60,11 @@ def source_sha(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"row_attn_kernel": ("attn_rows.hip", "cb_device.h", "cb_plan.h"),
-                  "row_attn_mfma_kernel": ("attn_decode_gqa.hip", "attn_decode_gqa.h", "cb_device.h", "cb_plan.h"),
-                  "prefill_kernel": ("attn_prefill.hip", "attn_prefill.h", "cb_device.h", "cb_plan.h")}
+# a kernel's traffic depends on its code and on the work lists the planner gives it
+KERNEL_SOURCES = {"row_attn_kernel": ("attn_rows.hip", "cb_device.h", "cb_plan.h", "plan.cpp"),
+                  "row_attn_mfma_kernel": ("attn_decode_gqa.hip", "attn_decode_gqa.h", "cb_device.h", "cb_plan.h",
+                                           "plan.cpp"),
+                  "prefill_kernel": ("attn_prefill.hip", "attn_prefill.h", "cb_device.h", "cb_plan.h", "plan.cpp")}
 
 
 def measured_traffic(kernel, workload):
