@@ -247,6 +247,8 @@ const char* cb_version(void);
  *                    over key ranges (partials merged by the combine pass); 0: never
  *   "prefill_split_tiles"  key tiles (64 keys) per split range, forcing splits in any step;
  *                    0 (default) = automatic
+ *   "decode_order"   1 (default): decode splits launched longest first; 0: in the order of
+ *                    their rows (longest row first)
  *   "mixed_launch"   1: a bf16 step with both prefill rows and grouped-query decode rows
  *                    (Hq/Hkv >= 4) runs its prefill tiles (128-row work-groups) and decode
  *                    waves in one launch, interleaved so that both kinds share every CU;

@@ -261,6 +261,8 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     g_tuning.prefill_split_tiles = value;
   } else if (std::strcmp(key, "mixed_launch") == 0) {
     g_tuning.mixed_launch = value != 0;
+  } else if (std::strcmp(key, "decode_order") == 0) {
+    g_tuning.decode_order = value != 0;
   } else if (std::strcmp(key, "mixed_order") == 0) {
     g_tuning.mixed_order = value != 0;
   } else if (std::strcmp(key, "stage_kernel") == 0) {

@@ -45,6 +45,7 @@ struct Tuning {
                                   // by the combine pass)
   int32_t prefill_split_tiles = 0;  // key tiles per split, forcing splits (tests); 0 = automatic
   int32_t mixed_launch = 0;       // 1: prefill tiles and matrix-core decode waves in one launch
+  int32_t decode_order = 1;       // 1: decode splits longest first; 0: rows longest first
   int32_t mixed_order = 0;        // 0: merge prefill and decode chunks in proportion to their
                                   // counts; 1: alternate them until one kind runs out
 };

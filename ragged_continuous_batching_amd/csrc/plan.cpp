@@ -247,6 +247,10 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves, b
                           static_cast<int32_t>(static_cast<int64_t>(k + 1) * nb / ns), row.kv_len, p.n_parts + k});
     p.n_parts += ns;
   }
+  // waves longest first (a long row's splits are shorter than a shorter row's single split)
+  if (g_tuning.decode_order == 1)
+    std::stable_sort(p.splits.begin(), p.splits.end(),
+                     [](const RowSplit& x, const RowSplit& y) { return x.blk_end - x.blk_begin > y.blk_end - y.blk_begin; });
 
   if (p.mixed) {
     // Chunks of one work-group per XCD. mixed_order 0: prefill and decode chunks merged in

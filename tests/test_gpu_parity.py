@@ -657,3 +657,21 @@ def test_requests_with_no_rows_in_every_entry_point():
     assert torch.equal(o1, o_ref)
     assert torch.equal(o2, o_ref)
     check(o1, oracle_full(wl, step), "bf16", "empty requests")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (4, 4)])
+def test_decode_rows_longest_first_order(hq, hkv):
+    """Decode splits in row order ("decode_order" = 0) instead of longest split first: the
+    same values within tolerance, bit-identical since each split's math does not depend on
+    its launch position."""
+    wl = small_workload("long_decode", hq, hkv, 128, "bf16")
+    outs = []
+    try:
+        for order in (1, 0):
+            cb.cb_set_tuning("decode_order", order)
+            run, step, batch, o = run_one_step(wl)
+            outs.append(o)
+    finally:
+        cb.cb_set_tuning("decode_order", 1)
+    assert torch.equal(outs[0], outs[1])
+    check(outs[1], oracle_full(wl, step), "bf16", f"decode rows-first order Hq={hq} Hkv={hkv}")
