@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+PROFILE_STEPS = 10            # untimed steps that time every kernel of a fixed step
 
 
 def algorithmic(wl, step):
@@ -157,8 +158,12 @@ def main(argv=None):
     ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                     help="cb_set_tuning(KEY, VALUE) before the run (repeatable)")
     ap.add_argument("--no-kernel-events", action="store_true",
-                    help="config 5: time the replay without the library's per-kernel timing events "
-                         "(no per-kernel durations or roofline)")
+                    help="time the steps without the library's per-kernel timing events (config 5: no "
+                         "per-kernel durations or roofline; fixed steps: the dominant kernel's duration "
+                         "comes from the untimed profiled steps)")
+    ap.add_argument("--all-kernel-events", action="store_true",
+                    help="config 5: an event pair around every kernel of the timed steps (default: only "
+                         "around the launches that stream the cache)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
                          "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
@@ -245,9 +250,29 @@ def main(argv=None):
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    host_ms.clear()
+    # Every kernel's time, from untimed steps with an event pair around each launch. Inside
+    # the timed steps only the dominant kernel carries events (each pair costs the stream
+    # about a microsecond or two).
     cb.cb_profile_reset()
+    cb.cb_profile_select(None)
     cb.cb_profile_enable(True)
+    for _ in range(PROFILE_STEPS):
+        one_step()
+    torch.cuda.synchronize()
+    cb.cb_profile_enable(False)
+    kernels = {}
+    for name, kid in cb.KERNELS.items():
+        ms, n = cb.cb_profile_read(kid)
+        if n:
+            kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "timed_steps": False}
+    cb.cb_profile_reset()
+    dominant = "prefill" if args.config in (0, 4) else "decode"
+    if dominant == "decode" and "mixed" in kernels:
+        dominant = "mixed"                 # prefill tiles and decode waves in one launch
+
+    host_ms.clear()
+    cb.cb_profile_select([cb.KERNELS[dominant]])
+    cb.cb_profile_enable(not args.no_kernel_events)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     keep = []
     torch.cuda.synchronize()
@@ -261,18 +286,14 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cb.cb_profile_enable(False)
+    cb.cb_profile_select(None)
     ms_per_step = wall * 1e3 / args.steps
     device_ms = ev0.elapsed_time(ev1) / args.steps
-    kernels = {}
-    for name, kid in cb.KERNELS.items():
-        ms, n = cb.cb_profile_read(kid)
-        if n:
-            kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n}
+    ms, n = cb.cb_profile_read(cb.KERNELS[dominant])
+    if n:
+        kernels[dominant] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "timed_steps": True}
     cb.cb_profile_reset()
 
-    dominant = "prefill" if args.config in (0, 4) else "decode"
-    if dominant == "decode" and "mixed" in kernels:
-        dominant = "mixed"                 # prefill tiles and decode waves in one launch
     avg_s = kernels[dominant]["avg_us"] * 1e-6
     if dominant == "mixed":
         achieved = alg["all"]["bytes"] / avg_s / 1e9
@@ -313,6 +334,8 @@ def main(argv=None):
         "device_ms_per_step": round(device_ms, 4),
         "host_build_ms_per_step": round(float(np.mean(host_ms)), 4),
         "kernels": kernels,
+        "kernel_events": (f"{dominant}: event pairs inside the timed steps; other kernels: "
+                          f"{PROFILE_STEPS} untimed steps with an event pair around every launch"),
         "algorithmic": alg,
         "attention_tokens_per_s": round(T / (sum(kernels[k]["avg_us"] for k in kernels if k != "append") * 1e-6), 1),
     }
@@ -469,6 +492,9 @@ def bench_trace(args):
         one(kstep)
     torch.cuda.synchronize()
     cb.cb_profile_reset()
+    # Only the launches that stream the cache carry events in the timed steps (each event
+    # pair costs the stream about a microsecond or two), unless every kernel is asked for.
+    cb.cb_profile_select(None if args.all_kernel_events else [cb.KERNELS["decode"], cb.KERNELS["mixed"]])
     cb.cb_profile_enable(not args.no_kernel_events)
     keep = []
     t0 = time.perf_counter()
@@ -482,6 +508,7 @@ def bench_trace(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     cb.cb_profile_enable(False)
+    cb.cb_profile_select(None)
     kernels = {}
     for name, kid in cb.KERNELS.items():
         ms, n = cb.cb_profile_read(kid)

@@ -273,6 +273,10 @@ int cb_profile_read(int kernel_id, double* total_ms, int64_t* launches);
  * values (ms) to host array ms_out and the number of recorded launches to *launches. */
 int cb_profile_launches(int kernel_id, float* ms_out, int64_t capacity, int64_t* launches);
 int cb_profile_reset(void);
+/* Restricts timing to the kernel ids whose bit (1 << id) is set in mask; the default, and
+ * mask = 0, time every kernel. Each event pair costs the stream about a microsecond or two,
+ * so a caller that times a whole step can select only the kernel it needs. */
+int cb_profile_select(uint32_t mask);
 const char* cb_kernel_name(int kernel_id);
 
 /* ---------------------------------------------------------------------------------------

@@ -86,6 +86,7 @@ def _load():
         "cb_qkv_project": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), ctypes.c_int32, P, P,
                                           P, P, P, P]),
         "cb_profile_reset": (ctypes.c_int, []),
+        "cb_profile_select": (ctypes.c_int, [ctypes.c_uint32]),
         "cb_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
         "cb_sched_create": (P, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
         "cb_sched_add": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
@@ -115,7 +116,7 @@ lib = _load()
 EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_attention", "cb_step_workspace_size",
             "cb_step_forward", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
-            "cb_profile_reset",
+            "cb_profile_reset", "cb_profile_select",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
             "cb_sched_set_preemption", "cb_linear", "cb_qkv_project", "cb_graph_create", "cb_graph_step",
@@ -247,6 +248,14 @@ def cb_set_tuning(key: str, value: int) -> int:
 
 def cb_profile_enable(on: bool) -> int:
     return _check(lib.cb_profile_enable(1 if on else 0))
+
+
+def cb_profile_select(kernel_ids=None) -> int:
+    """Times only the given kernel ids while profiling is on (None: every kernel)."""
+    mask = 0
+    for k in kernel_ids or ():
+        mask |= 1 << int(k)
+    return _check(lib.cb_profile_select(mask))
 
 
 def cb_profile_launches(kernel_id: int) -> np.ndarray:

@@ -30,6 +30,7 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_mask = ~0u;          // kernel ids (bits) that get an event pair
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;     // events of earlier records, reused (no create per launch)
 
@@ -51,7 +52,7 @@ struct ProfScope {
   hipEvent_t start = nullptr, stop = nullptr;
   ProfScope(int k, hipStream_t s) : kernel(k), stream(s) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on) return;
+    if (!g_prof_on || !((g_prof_mask >> k) & 1u)) return;
     start = pooled_event();
     stop = pooled_event();
     if (!start || !stop) {
@@ -292,6 +293,12 @@ extern "C" const char* cb_kernel_name(int k) {
 extern "C" int cb_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return CB_OK;
+}
+
+extern "C" int cb_profile_select(uint32_t mask) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_mask = mask ? mask : ~0u;
   return CB_OK;
 }
 

@@ -551,6 +551,29 @@ def test_mixed_launch_matches_two_launches_and_oracle(name, hq, hkv, d, order):
     check(outs[1], oracle_full(wl, step), "bf16", f"mixed launch {name} Hq={hq} Hkv={hkv} D={d}")
 
 
+def test_profile_select_times_only_the_selected_kernels():
+    """cb_profile_select restricts the event pairs to the selected kernel ids; None restores
+    every kernel. The outputs do not depend on it."""
+    wl = small_workload("mixed", 8, 8, 128, "bf16")
+    outs, launched = [], []
+    try:
+        for sel in ([cb.KERNELS["decode"]], None):
+            cb.cb_profile_reset()
+            cb.cb_profile_select(sel)
+            cb.cb_profile_enable(True)
+            run, step, batch, o = run_one_step(wl)
+            cb.cb_profile_enable(False)
+            launched.append({k: cb.cb_profile_read(v)[1] for k, v in cb.KERNELS.items()})
+            outs.append(o)
+    finally:
+        cb.cb_profile_enable(False)
+        cb.cb_profile_select(None)
+        cb.cb_profile_reset()
+    assert launched[0] == {k: int(k == "decode") for k in cb.KERNELS}, launched[0]
+    assert launched[1]["append"] >= 1 and launched[1]["decode"] == 1 and launched[1]["prefill"] == 1, launched[1]
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_mixed_launch_trace_replay():
     """The first 150 steps of the scheduler trace with the mixed launch; sampled rows of
     every 30th step against the oracle."""
