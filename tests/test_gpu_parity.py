@@ -98,6 +98,9 @@ SMALL = {
     "mixed": [(37, 37, 1), (0, 1, 0), (None, 130, 0), (5, 20, 0), (16, 16, 1), (None, 1, 0), (200, 300, 0)],
     "tile_edges": [(None, 129, 0), (63, 64 + 63 + 65, 0), (127, 127, 1), (None, 2, 0), (15, 15 + 17, 0)],
     "long_decode": [(2100, 2100, 1), (777, 777, 1), (None, 300, 0)],
+    # a 256-row chunk after 4000 cached tokens: few, long prefill tiles, so the automatic
+    # choice takes 256-row work-groups split over key ranges
+    "late_chunk": [(4000, 4256, 0), (1500, 1500, 1), (None, 40, 0)],
 }
 
 
