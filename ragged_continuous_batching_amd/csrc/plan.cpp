@@ -95,10 +95,14 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves, b
   p.prefill_waves = p.mixed ? 4 : force_waves ? force_waves : g_tuning.prefill_waves;
   if (p.prefill_waves == 0) {
     // 256-row work-groups read each key/value tile once for twice the rows, but a CU holds
-    // only one of them (registers). Take them when there are enough to fill every CU twice,
-    // and also when there are fewer than CUs but long ones (32+ key tiles on average): the
-    // split over key ranges then makes the work-groups, and the halved key/value traffic
-    // counts (a late 256-row chunk after 16k cached tokens: prefill 104.7 -> 95.5 us).
+    // only one of them (registers), so nothing hides a work-group's start (its query rows
+    // and first tiles) and end. Take them when there are enough to fill every CU twice and
+    // they are long (16+ key tiles on average: the 2048-token chunks with long contexts);
+    // short fresh chunks (the trace replay) run 2% faster as 128-row work-groups, two per
+    // CU. Also take them when there are fewer than CUs but long ones (32+ key tiles on
+    // average): the split over key ranges then makes the work-groups, and the halved
+    // key/value traffic counts (a late 256-row chunk after 16k cached tokens: prefill
+    // 104.7 -> 95.5 us).
     int64_t items256 = 0, tiles256 = 0;
     for (int32_t r = 0; r < b->num_reqs; ++r) {
       const int32_t q = b->h_cu_q_lens[r + 1] - b->h_cu_q_lens[r], c = b->h_ctx_lens[r];
@@ -109,7 +113,8 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves, b
       }
     }
     const bool few_long = items256 < kNumCUs && tiles256 >= 32 * items256 && g_tuning.prefill_split;
-    p.prefill_waves = items256 >= 2 * kNumCUs || few_long ? 8 : 4;
+    const bool many_long = items256 >= 2 * kNumCUs && tiles256 >= 16 * items256;
+    p.prefill_waves = many_long || few_long ? 8 : 4;
   }
 
   // rows that take the split-K path, longest first
