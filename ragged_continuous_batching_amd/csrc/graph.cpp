@@ -323,7 +323,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   const int64_t n16 = static_cast<int64_t>(l.stage_bytes / 16);
   auto blocks = [](int64_t n, int64_t per) { return static_cast<unsigned>(std::max<int64_t>(1, (n + per - 1) / per)); };
   if ((st = set_grid(sl, kNodeStage, dim3(std::min(blocks(n16, 256), 1024u)))) ||
-      (st = set_grid(sl, kNodeAppend, dim3(blocks(num_tokens, 16), blocks(sh->num_kv_heads, 4)))) ||
+      (st = set_grid(sl, kNodeAppend, append_grid(num_tokens, sh->num_kv_heads, elem_bytes(sh), sh->head_dim))) ||
       (st = set_grid(sl, kNodePrefill, dim3(blocks(n_pre, 1)))) ||
       (st = set_grid(sl, kNodeDecode, dim3(blocks(n_rows, 4)))) ||
       (st = set_grid(sl, kNodeCombine, dim3(blocks(static_cast<int64_t>(n_comb) * sh->num_q_heads, 4)))))

@@ -156,12 +156,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   }
 }
 
+dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim) {
+  const int h = elem_bytes == 2 ? (head_dim == 128 ? append_heads<2, 128>() : append_heads<2, 64>())
+                                : (head_dim == 128 ? append_heads<4, 128>() : append_heads<4, 64>());
+  return dim3(static_cast<unsigned>((num_tokens + 15) / 16), static_cast<unsigned>((num_kv_heads + h - 1) / h));
+}
+
 template <int ES, int D>
 static hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  constexpr int H = append_heads<ES, D>();
-  hipLaunchKernelGGL((kv_append_kernel<ES, D>), dim3((a.num_tokens + 15) / 16, (a.num_kv_heads + H - 1) / H),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL((kv_append_kernel<ES, D>), append_grid(a.num_tokens, a.num_kv_heads, ES, D), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 
