@@ -159,7 +159,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim) {
   const int h = elem_bytes == 2 ? (head_dim == 128 ? append_heads<2, 128>() : append_heads<2, 64>())
                                 : (head_dim == 128 ? append_heads<4, 128>() : append_heads<4, 64>());
-  return dim3(static_cast<unsigned>((num_tokens + 15) / 16), static_cast<unsigned>((num_kv_heads + h - 1) / h));
+  // at least one work-group in each dimension (a captured step may replay with no rows; the
+  // kernel exits for rows and heads past the end)
+  const int64_t x = (num_tokens + 15) / 16, y = (num_kv_heads + h - 1) / h;
+  return dim3(static_cast<unsigned>(x > 0 ? x : 1), static_cast<unsigned>(y > 0 ? y : 1));
 }
 
 template <int ES, int D>
