@@ -222,9 +222,10 @@ const char* cb_version(void);
 /* Tuning knobs (process-wide, host-side, read by every later call when it plans its launches;
  * a captured cb_graph keeps the kernels it was captured with). Set them before issuing work:
  * changing a knob while another thread is inside a library call is a data race. Keys:
- *   "split_blocks"   KV blocks per split of a decode row, at most 64; 0 = automatic (default)
+ *   "split_blocks"   KV blocks per split of a decode row, at most 1024; 0 = automatic
+ *                    (default)
  *   "target_waves"   automatic split sizing aims for at least this many wave items; 0
- *                    (default) = 8192 for the vector-ALU decode kernel, 4096 for the
+ *                    (default) = 4096 for the vector-ALU decode kernel, 2048 for the
  *                    matrix-core one
  *   "overlap_prefill" 1 = run prefill tiles on an internal side stream (forked from and
  *                    joined back to `stream`) concurrently with decode rows; 0 (default)

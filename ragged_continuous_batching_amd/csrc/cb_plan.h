@@ -65,7 +65,7 @@ constexpr int kDescBytes = 256;        // the header's slot at the head of the w
 
 constexpr int kBlockSize = 16;         // KV positions per physical block
 constexpr int kPrefillKeys = 64;       // keys per prefill K/V tile (4 blocks)
-constexpr int kMaxSplitBlocks = 64;    // blocks per decode split (one block id per lane)
+constexpr int kMaxSplitBlocks = 1024;  // blocks per decode split at most (16k positions)
 constexpr int kNumCUs = 256;           // compute units of the target GPU (MI355X)
 
 struct AppendArgs {
