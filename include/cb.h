@@ -118,6 +118,27 @@ int cb_kv_append(const cb_shape* shape, const cb_batch* batch, const void* k_new
  * ------------------------------------------------------------------------------------- */
 size_t cb_ragged_attention_workspace_size(const cb_shape* shape, const cb_batch* batch);
 
+/* What cb_ragged_attention would launch for `batch` (host-side planning only: reads the
+ * host mirrors h_cu_q_lens and h_ctx_lens, touches no device memory, needs no GPU). For
+ * tests and tools that check the planner's choices; the fields are counts of the launch
+ * lists, with the tuning knobs in effect at the call. */
+typedef struct {
+  int32_t prefill_rows;          /* query rows per prefill work-group: 128, 256, or 0 (none) */
+  int32_t prefill_items;         /* prefill work-groups, empty launch-order slots included */
+  int32_t prefill_split_items;   /* of those, items covering one key range of a split tile */
+  int32_t decode_splits;         /* row splits of the split-K path (decode rows; fp32 prefill rows) */
+  int32_t decode_items;          /* decode waves: splits x kv heads x query-head groups */
+  int32_t split_blocks;          /* split length the sizing chose (KV blocks) */
+  int32_t split_min_blocks;      /* shortest and longest split, in blocks (0 if none) */
+  int32_t split_max_blocks;
+  int32_t longest_first;         /* 1: splits are listed in non-increasing length */
+  int32_t matrix_core_decode;    /* 1: the split-K rows run on the matrix-core kernel */
+  int32_t combine_rows;          /* rows merged by the combine pass */
+  int32_t mixed;                 /* 1: prefill tiles and decode waves share one launch */
+} cb_plan_info;
+/* Returns CB_OK, or the error cb_ragged_attention would return for the shape and batch. */
+int cb_plan_describe(const cb_shape* shape, const cb_batch* batch, cb_plan_info* out);
+
 int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void* q,
                         const void* k_cache, const void* v_cache, float scale, void* o,
                         void* workspace, size_t workspace_bytes, void* stream);

@@ -47,6 +47,12 @@ class cb_batch(ctypes.Structure):
                 ("h_cu_q_lens", ctypes.c_void_p), ("h_ctx_lens", ctypes.c_void_p)]
 
 
+class cb_plan_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "prefill_rows", "prefill_items", "prefill_split_items", "decode_splits", "decode_items", "split_blocks",
+        "split_min_blocks", "split_max_blocks", "longest_first", "matrix_core_decode", "combine_rows", "mixed")]
+
+
 class cb_step(ctypes.Structure):
     _fields_ = [("num_reqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("max_blocks_per_req", ctypes.c_int32),
                 ("num_decode", ctypes.c_int32), ("req_ids", _i64p), ("cu_q_lens", _i32p), ("ctx_lens", _i32p),
@@ -70,6 +76,8 @@ def _load():
     sig = {
         "cb_kv_append": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), P, P, P, P, P]),
         "cb_ragged_attention_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch)]),
+        "cb_plan_describe": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch),
+                                            ctypes.POINTER(cb_plan_info)]),
         "cb_ragged_attention": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), P, P, P,
                                                ctypes.c_float, P, P, ctypes.c_size_t, P]),
         "cb_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32,
@@ -113,7 +121,8 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_ragged_attention", "cb_step_workspace_size",
+EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_plan_describe", "cb_ragged_attention",
+            "cb_step_workspace_size",
             "cb_step_forward", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
             "cb_profile_reset", "cb_profile_select",
@@ -159,6 +168,13 @@ def cb_kv_append(shape: cb_shape, batch: cb_batch, k_new, v_new, k_cache, v_cach
 
 def cb_ragged_attention_workspace_size(shape: cb_shape, batch: cb_batch) -> int:
     return int(lib.cb_ragged_attention_workspace_size(ctypes.byref(shape), ctypes.byref(batch)))
+
+
+def cb_plan_describe(shape: cb_shape, batch: cb_batch) -> dict:
+    """The launch plan cb_ragged_attention would use for `batch` (host-side, no GPU)."""
+    info = cb_plan_info()
+    _check(lib.cb_plan_describe(ctypes.byref(shape), ctypes.byref(batch), ctypes.byref(info)))
+    return {name: int(getattr(info, name)) for name, _ in cb_plan_info._fields_}
 
 
 def cb_ragged_attention(shape: cb_shape, batch: cb_batch, q, k_cache, v_cache, scale: float, o, workspace,

@@ -381,6 +381,35 @@ extern "C" size_t cb_ragged_attention_workspace_size(const cb_shape* shape, cons
   return p.total;
 }
 
+extern "C" int cb_plan_describe(const cb_shape* shape, const cb_batch* batch, cb_plan_info* out) {
+  if (!out) return fail(CB_ERR_INVALID_ARG, "cb_plan_describe: out is null");
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_batch(shape, batch))) return st;
+  *out = cb_plan_info{};
+  if (batch->num_tokens == 0) return CB_OK;
+  Plan p;
+  make_plan(shape, batch, p);
+  out->prefill_rows = p.prefill.empty() ? 0 : 32 * p.prefill_waves;
+  out->prefill_items = static_cast<int32_t>(p.prefill.size());
+  for (const PrefillItem& it : p.prefill)
+    if (it.req >= 0 && it.part_base >= 0) ++out->prefill_split_items;
+  out->decode_splits = static_cast<int32_t>(p.splits.size());
+  out->decode_items = static_cast<int32_t>(p.splits.size()) * shape->num_kv_heads * p.n_sub;
+  out->split_blocks = p.splits.empty() ? 0 : p.split_blocks;
+  out->longest_first = 1;
+  for (size_t i = 0; i < p.splits.size(); ++i) {
+    const int32_t len = p.splits[i].blk_end - p.splits[i].blk_begin;
+    out->split_min_blocks = i == 0 ? len : std::min(out->split_min_blocks, len);
+    out->split_max_blocks = std::max(out->split_max_blocks, len);
+    if (i > 0 && len > p.splits[i - 1].blk_end - p.splits[i - 1].blk_begin) out->longest_first = 0;
+  }
+  out->matrix_core_decode = !p.splits.empty() && p.mfma_decode;
+  out->combine_rows = static_cast<int32_t>(p.combine.size());
+  out->mixed = p.mixed;
+  return CB_OK;
+}
+
 extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void* q,
                                    const void* k_cache, const void* v_cache, float scale, void* o,
                                    void* workspace, size_t workspace_bytes, void* stream) {

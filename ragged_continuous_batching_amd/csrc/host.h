@@ -78,6 +78,7 @@ struct Plan {
   bool mfma_decode = false;  // decode rows on the MFMA kernel
   int prefill_waves = 4;     // waves (x 32 query rows) per prefill work-group
   int n_sub = 1;         // decode waves per kv head
+  int32_t split_blocks = 0;  // split length chosen for the split-K rows
   bool mixed = false;    // prefill tiles and decode waves in one launch (order below)
   std::vector<int32_t> order;
   size_t off_combine = 0, off_prefill = 0, off_order = 0, plan_bytes = 0, off_part_o = 0, off_part_ml = 0,

@@ -249,6 +249,7 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves, b
     split = static_cast<int32_t>(std::clamp<int64_t>((units + target - 1) / target, 4, kMaxSplitBlocks));
   }
   split = std::min(split, kMaxSplitBlocks);
+  p.split_blocks = split;
   for (const Row& row : rows) {
     const int32_t nb = ceil_div(row.kv_len, kBlockSize);
     const int32_t ns = ceil_div(nb, split);

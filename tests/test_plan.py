@@ -1,0 +1,145 @@
+"""The launch planner's choices, from host metadata only (cb_plan_describe; no GPU).
+
+Each test builds a batch from (query rows, cached tokens) pairs, with placeholder device
+pointers (the planner reads only the host mirrors), and checks one rule of the planner:
+the prefill work-group size, the split over key ranges, the decode split sizing and its
+near-equal lengths, the longest-first order and the kernel choice.
+"""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+from ragged_continuous_batching_amd import cb
+
+_KEEP = []
+
+
+def batch(reqs, block_size=16):
+    """cb_batch over host mirrors for [(q_len, ctx_len), ...]."""
+    q = np.array([r[0] for r in reqs], dtype=np.int32)
+    c = np.array([r[1] for r in reqs], dtype=np.int32)
+    cu = np.zeros(len(reqs) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q)
+    maxb = max(1, max(-(-(int(a) + int(b)) // block_size) for a, b in zip(q, c)))
+    _KEEP.append((cu, c))
+    fake = ctypes.c_void_p(256)        # never dereferenced: the planner reads host mirrors
+    return cb.cb_batch(len(reqs), int(cu[-1]), maxb, fake, fake, fake, cu.ctypes.data, c.ctypes.data)
+
+
+def describe(reqs, hq, hkv, d=128, dtype="bf16", **tune):
+    shape = cb.make_shape(hq, hkv, d, 1 << 24, dtype)
+    try:
+        for k, v in tune.items():
+            cb.cb_set_tuning(k, v)
+        return cb.cb_plan_describe(shape, batch(reqs))
+    finally:
+        defaults = {"split_blocks": 0, "target_waves": 0, "prefill_waves": 0, "decode_order": 1,
+                    "mixed_launch": 0, "prefill_split_tiles": 0, "decode_mfma": 1}
+        for k in tune:
+            cb.cb_set_tuning(k, defaults[k])
+
+
+def test_long_chunks_take_256_row_work_groups():
+    """Four 2048-row chunks with long contexts (the chunked-prefill-heavy step): 1024
+    row tiles of 256 rows averaging about 106 key tiles, so 256-row work-groups."""
+    info = describe([(2048, 2048), (2048, 6144), (2048, 14336), (2048, 0)], 32, 32)
+    assert info["prefill_rows"] == 256
+    assert info["decode_splits"] == 0 and info["prefill_split_items"] == 0
+
+
+def test_short_fresh_chunks_take_128_row_work_groups():
+    """Many short fresh prompts (the trace's steps): enough 256-row tiles, but only about 4
+    key tiles each, so 128-row work-groups, two per CU."""
+    info = describe([(256, 0)] * 16 + [(1, 700)] * 8, 64, 8)
+    assert info["prefill_rows"] == 128
+
+
+def test_late_chunk_takes_256_rows_split_over_key_ranges():
+    """One 256-row chunk after 16384 cached tokens: few but long row tiles, so 256-row
+    work-groups split over key ranges (about one per CU)."""
+    info = describe([(256, 16384)], 32, 32)
+    assert info["prefill_rows"] == 256
+    assert info["prefill_split_items"] > 0
+    assert info["combine_rows"] == 256        # every row of the chunk merges its ranges
+
+
+def test_mixed_step_keeps_128_rows_and_decode_on_vector_alu():
+    """The Llama-2-7B-shaped step (64 decodes, two 992-row chunks, Hq = Hkv): 128-row
+    prefill work-groups, unsplit key ranges, decode rows on the vector-ALU kernel."""
+    rng = np.random.default_rng(1)
+    reqs = [(1, int(c)) for c in rng.integers(512, 4097, size=64)] + [(992, 1024), (992, 0)]
+    info = describe(reqs, 32, 32)
+    assert info["prefill_rows"] == 128 and info["prefill_split_items"] == 0
+    assert info["decode_splits"] >= 64 and info["matrix_core_decode"] == 0
+    assert info["decode_items"] == info["decode_splits"] * 32
+
+
+def test_grouped_query_decode_on_matrix_cores():
+    """Four or more query heads per kv head: decode rows on the matrix-core kernel, one wave
+    per (split, kv head) with up to 8 heads."""
+    info = describe([(1, 2000 + 37 * i) for i in range(64)], 32, 8)
+    assert info["matrix_core_decode"] == 1
+    assert info["decode_items"] == info["decode_splits"] * 8
+
+
+def test_split_sizing_targets_the_wave_count():
+    """Automatic split length = ceil(row-blocks x kv heads / target), target 2048 wave items
+    for the matrix-core kernel, at least 4 and at most 1024 blocks."""
+    ctx = [16 * 200 - 1] * 256                   # 200 blocks per row with the new token
+    info = describe([(1, c) for c in ctx], 32, 8)
+    units = 256 * 200 * 8
+    assert info["split_blocks"] == min(1024, max(4, math.ceil(units / 2048)))
+    # a smaller target gives longer splits
+    longer = describe([(1, c) for c in ctx], 32, 8, target_waves=512)
+    assert longer["split_blocks"] > info["split_blocks"]
+
+
+def test_splits_are_near_equal():
+    """A 209-block row at split length 64 takes 4 splits of 53/52/52/52 blocks, not
+    64/64/64/17 (no tail sliver)."""
+    info = describe([(1, 16 * 209 - 1)], 32, 8, split_blocks=64)
+    assert info["decode_splits"] == 4
+    assert (info["split_min_blocks"], info["split_max_blocks"]) == (52, 53)
+    assert info["combine_rows"] == 1
+
+
+def test_splits_launch_longest_first():
+    """decode_order = 1 lists the splits in non-increasing length; a long row's splits can be
+    shorter than a short row's single split, so ordering rows (decode_order = 0) does not
+    order the splits."""
+    reqs = [(1, 16 * 130 - 1), (1, 16 * 70 - 1), (1, 16 * 20 - 1)]
+    assert describe(reqs, 32, 8, split_blocks=64)["longest_first"] == 1
+    by_rows = describe(reqs, 32, 8, split_blocks=64, decode_order=0)
+    assert by_rows["longest_first"] == 0         # 43/43/44 (130 blocks) then 35/35 (70): not sorted by split
+
+
+def test_mixed_launch_needs_both_kinds_of_rows():
+    """With mixed_launch set, a bf16 step with prefill chunks and matrix-core decode rows
+    takes one launch; a decode-only step does not."""
+    both = describe([(300, 0), (1, 900), (1, 2000)], 16, 2, mixed_launch=1)
+    assert both["mixed"] == 1 and both["prefill_rows"] == 128
+    decode_only = describe([(1, 900), (1, 2000)], 16, 2, mixed_launch=1)
+    assert decode_only["mixed"] == 0
+
+
+def test_fp32_prefill_rows_take_the_split_k_path():
+    """fp32 steps have no MFMA prefill tiles: every row of a chunk is a split-K row."""
+    info = describe([(40, 100), (1, 50)], 4, 2, d=64, dtype="f32")
+    assert info["prefill_rows"] == 0 and info["prefill_items"] == 0
+    assert info["decode_splits"] >= 41
+
+
+def test_empty_batch():
+    shape = cb.make_shape(8, 2, 128, 1024, "bf16")
+    info = cb.cb_plan_describe(shape, cb.cb_batch(0, 0, 0, None, None, None, None, None))
+    assert all(v == 0 for v in info.values())
+
+
+def test_rejects_a_batch_that_overflows_its_block_table():
+    shape = cb.make_shape(8, 2, 128, 1024, "bf16")
+    b = batch([(10, 100)])
+    b.max_blocks_per_req = 2                     # 110 positions need 7 blocks
+    with pytest.raises(cb.CbError):
+        cb.cb_plan_describe(shape, b)
