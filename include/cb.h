@@ -89,9 +89,9 @@ typedef struct {
 } cb_batch;
 
 /* ---------------------------------------------------------------------------------------
- * KV append (zhangchitc "continuous-batching", section "Inside the kernel": the new keys
- * and values are written into the KV cache, each into its own request's entry, before
- * attention reads them back).
+ * KV append (zhangchitc "continuous-batching", section "Inside the kernel": a step's new
+ * keys and values go into the cache slots of the request they belong to, and attention
+ * then reads them back from there).
  *   k_new, v_new  device [num_tokens, Hkv, head_dim], packed like Q
  *   k_cache, v_cache  device, layout in cb_shape; updated in place
  * Row t of request r (position p = ctx_lens[r] + t - cu_q_lens[r]) is copied bit for bit
@@ -253,8 +253,6 @@ const char* cb_version(void);
  *                    runs them one after the other on `stream`
  *   "xcds"           number of XCDs work-groups are dispatched over round-robin (8 on
  *                    MI355X); prefill tiles that share keys are placed on one XCD
- *   "prefill_touch"  1 = the prefill kernel also loads one dword per cache line of the key
- *                    tile two steps ahead (warms L2); 0 (default) = off
  *   "decode_mfma"    1 (default) = decode rows of bf16 models with 4 or more query heads per
  *                    kv head use the matrix-core kernel; 0 = the vector-ALU kernel
  *   "decode_group"   most query heads of one kv head that a decode wave handles (1, 2, 4
@@ -266,6 +264,10 @@ const char* cb_version(void);
  *   "prefill_waves"  waves per bf16 prefill work-group: 4 (128 query rows, two work-groups
  *                    per CU), 8 (256 rows, one per CU), or 0 (default) = 8 when a step has at
  *                    least 2 x 256 such work-groups, else 4
+ *   "prefill_snake"  1 (default): within each XCD's queue of prefill work-groups, every
+ *                    other round of one work-group per CU is reversed, so a CU that got a
+ *                    long work-group in one round gets a short one in the next; 0: the
+ *                    queues stay longest first
  *   "prefill_split"  1 (default): when a bf16 step has fewer prefill work-groups than the
  *                    GPU has work-group slots, prefill tiles with long key walks are split
  *                    over key ranges (partials merged by the combine pass); 0: never
@@ -282,6 +284,9 @@ const char* cb_version(void);
  *                    kind runs out
  * Returns CB_ERR_INVALID_ARG for an unknown key or a negative value. */
 int cb_set_tuning(const char* key, int32_t value);
+/* Current value of one tuning key (as stored: boolean keys read 0 or 1) into *value.
+ * Returns CB_ERR_INVALID_ARG for an unknown key or a NULL value pointer. */
+int cb_get_tuning(const char* key, int32_t* value);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel timing (hipEvents recorded on the stream each kernel is launched on).

@@ -55,14 +55,16 @@ def attend(q, keys, values, positions, scale):
     group = hq // hkv
     visible = np.arange(L)[None, :] <= positions[:, None]          # [n, L] boolean mask
     out = np.zeros((n, hq, d), dtype=F64)
-    for h in range(hq):
-        g = h // group
-        s = scale * (q[:, h, :] @ keys[:, g, :].T)                 # [n, L] scores
-        s = np.where(visible, s, -np.inf)
-        s = s - s.max(axis=1, keepdims=True)
-        p = np.exp(s)
-        p = p / p.sum(axis=1, keepdims=True)                       # row-wise softmax
-        out[:, h, :] = p @ values[:, g, :]
+    for g in range(hkv):
+        kg = np.ascontiguousarray(keys[:, g, :])                    # [L, D] kv head g, read by
+        vg = np.ascontiguousarray(values[:, g, :])                  # query heads h // group == g
+        for h in range(g * group, (g + 1) * group):
+            s = scale * (q[:, h, :] @ kg.T)                         # [n, L] scores
+            s = np.where(visible, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)                   # row-wise softmax
+            out[:, h, :] = p @ vg
     return out
 
 

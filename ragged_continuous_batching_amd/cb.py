@@ -87,6 +87,7 @@ def _load():
         "cb_last_error": (ctypes.c_char_p, []),
         "cb_version": (ctypes.c_char_p, []),
         "cb_set_tuning": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
+        "cb_get_tuning": (ctypes.c_int, [ctypes.c_char_p, _i32p]),
         "cb_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "cb_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), _i64p]),
         "cb_profile_launches": (ctypes.c_int, [ctypes.c_int, P, ctypes.c_int64, _i64p]),
@@ -124,7 +125,7 @@ lib = _load()
 EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_plan_describe", "cb_ragged_attention",
             "cb_step_workspace_size",
             "cb_step_forward", "cb_last_error",
-            "cb_version", "cb_set_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
+            "cb_version", "cb_set_tuning", "cb_get_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
             "cb_profile_reset", "cb_profile_select",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
@@ -260,6 +261,32 @@ def cb_version() -> str:
 
 def cb_set_tuning(key: str, value: int) -> int:
     return _check(lib.cb_set_tuning(key.encode(), int(value)))
+
+
+def cb_get_tuning(key: str) -> int:
+    v = ctypes.c_int32(0)
+    _check(lib.cb_get_tuning(key.encode(), ctypes.byref(v)))
+    return int(v.value)
+
+
+class tuned:
+    """Context manager: sets tuning keys for the duration of a block and restores the values
+    they had before (``with tuned(overlap_prefill=1): ...``)."""
+
+    def __init__(self, **keys):
+        self.keys = keys
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.keys.items():
+            self.saved[k] = cb_get_tuning(k)
+            cb_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            cb_set_tuning(k, v)
+        return False
 
 
 def cb_profile_enable(on: bool) -> int:

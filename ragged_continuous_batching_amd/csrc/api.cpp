@@ -173,7 +173,7 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
   int st = CB_OK;
   // Prefill tiles (MFMA-bound) and decode rows (HBM-bound) touch disjoint rows of O. With
   // "overlap_prefill" set, the prefill kernel runs on a side stream forked from `stream` and
-  // joined back before the call returns, so the two can share the device. It is off by
+  // joined back before the combine pass, so the two can share the device. It is off by
   // default: measured on config 2, co-resident prefill work-groups slowed the decode kernel
   // more than the overlap saved.
   hipStream_t ps = s;
@@ -188,7 +188,7 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
   const PrefillArgs pa{q, k_cache, v_cache, o, reinterpret_cast<const PrefillItem*>(ws + p.off_prefill),
                        batch->cu_q_lens, batch->ctx_lens, batch->block_tables, static_cast<int32_t>(p.prefill.size()),
                        shape->num_q_heads, shape->num_kv_heads, batch->max_blocks_per_req, shape->num_blocks,
-                       scale_log2, g_tuning.prefill_touch, nullptr,
+                       scale_log2, nullptr,
                        reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml)};
   const RowArgs ra{q, k_cache, v_cache, o,
                    reinterpret_cast<float*>(ws + p.off_part_o), reinterpret_cast<float*>(ws + p.off_part_ml),
@@ -211,6 +211,13 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
       e = p.mfma_decode ? launch_rows_mfma(ra, shape->head_dim, s) : launch_rows(ra, eb, shape->head_dim, p.group, s);
     }
   }
+  // The side stream is joined back before the combine pass: split prefill tiles leave
+  // partials that the combine merges, so it must follow the prefill kernel as well as the
+  // decode kernel.
+  if (fork) {
+    if (hipEventRecord(side->join, ps) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+      return fail(CB_ERR_HIP, "cb_ragged_attention: join failed");
+  }
   if (e == hipSuccess && !p.combine.empty()) {
     CombineArgs ca{o, reinterpret_cast<const float*>(ws + p.off_part_o),
                    reinterpret_cast<const float*>(ws + p.off_part_ml),
@@ -218,10 +225,6 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
                    shape->num_q_heads};
     ProfScope prof(CB_KERNEL_COMBINE, s);
     e = launch_combine(ca, eb, shape->head_dim, s);
-  }
-  if (fork) {
-    if (hipEventRecord(side->join, ps) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
-      return fail(CB_ERR_HIP, "cb_ragged_attention: join failed");
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_ragged_attention: launch failed: %s", hipGetErrorString(e));
   return CB_OK;
@@ -236,45 +239,67 @@ extern "C" const char* cb_last_error(void) { return last_error().c_str(); }
 
 extern "C" const char* cb_version(void) { return "cb 0.1 gfx950"; }
 
+namespace {
+
+// The tuning keys: name, field, and the values a key accepts (checked by cb_set_tuning;
+// boolean keys store value != 0).
+struct TuningKey {
+  const char* name;
+  int32_t Tuning::*field;
+  enum Kind { kCount, kBool, kXcds, kWaves, kGroup } kind;
+};
+constexpr TuningKey kTuningKeys[] = {
+    {"split_blocks", &Tuning::split_blocks, TuningKey::kCount},
+    {"target_waves", &Tuning::target_waves, TuningKey::kCount},
+    {"overlap_prefill", &Tuning::overlap_prefill, TuningKey::kBool},
+    {"xcds", &Tuning::xcds, TuningKey::kXcds},
+    {"decode_group", &Tuning::decode_group, TuningKey::kGroup},
+    {"decode_mfma", &Tuning::decode_mfma, TuningKey::kBool},
+    {"stage_kernel", &Tuning::stage_kernel, TuningKey::kBool},
+    {"prefill_snake", &Tuning::prefill_snake, TuningKey::kBool},
+    {"prefill_waves", &Tuning::prefill_waves, TuningKey::kWaves},
+    {"prefill_split", &Tuning::prefill_split, TuningKey::kBool},
+    {"prefill_split_tiles", &Tuning::prefill_split_tiles, TuningKey::kCount},
+    {"mixed_launch", &Tuning::mixed_launch, TuningKey::kBool},
+    {"decode_order", &Tuning::decode_order, TuningKey::kBool},
+    {"mixed_order", &Tuning::mixed_order, TuningKey::kBool},
+};
+
+const TuningKey* find_tuning_key(const char* key) {
+  if (!key) return nullptr;
+  for (const TuningKey& k : kTuningKeys)
+    if (std::strcmp(key, k.name) == 0) return &k;
+  return nullptr;
+}
+
+}  // namespace
+
 extern "C" int cb_set_tuning(const char* key, int32_t value) {
-  if (!key || value < 0) return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: bad key or value");
-  if (std::strcmp(key, "split_blocks") == 0) {
-    g_tuning.split_blocks = value;
-  } else if (std::strcmp(key, "target_waves") == 0) {
-    g_tuning.target_waves = value;
-  } else if (std::strcmp(key, "overlap_prefill") == 0) {
-    g_tuning.overlap_prefill = value != 0;
-  } else if (std::strcmp(key, "xcds") == 0) {
-    g_tuning.xcds = std::max<int32_t>(1, value);
-  } else if (std::strcmp(key, "prefill_touch") == 0) {
-    g_tuning.prefill_touch = value != 0;
-  } else if (std::strcmp(key, "decode_mfma") == 0) {
-    g_tuning.decode_mfma = value != 0;
-  } else if (std::strcmp(key, "prefill_waves") == 0) {
-    if (value != 0 && value != 4 && value != 8)
-      return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: prefill_waves must be 0, 4 or 8");
-    g_tuning.prefill_waves = value;
-  } else if (std::strcmp(key, "prefill_snake") == 0) {
-    g_tuning.prefill_snake = value != 0;
-  } else if (std::strcmp(key, "prefill_split") == 0) {
-    g_tuning.prefill_split = value != 0;
-  } else if (std::strcmp(key, "prefill_split_tiles") == 0) {
-    g_tuning.prefill_split_tiles = value;
-  } else if (std::strcmp(key, "mixed_launch") == 0) {
-    g_tuning.mixed_launch = value != 0;
-  } else if (std::strcmp(key, "decode_order") == 0) {
-    g_tuning.decode_order = value != 0;
-  } else if (std::strcmp(key, "mixed_order") == 0) {
-    g_tuning.mixed_order = value != 0;
-  } else if (std::strcmp(key, "stage_kernel") == 0) {
-    g_tuning.stage_kernel = value != 0;
-  } else if (std::strcmp(key, "decode_group") == 0) {
-    if (value != 1 && value != 2 && value != 4 && value != 8)
-      return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: decode_group must be 1, 2, 4 or 8");
-    g_tuning.decode_group = value;
-  } else {
-    return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: unknown key '%s'", key);
+  const TuningKey* k = find_tuning_key(key);
+  if (!k) return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: unknown key '%s'", key ? key : "(null)");
+  if (value < 0) return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: negative value for '%s'", k->name);
+  switch (k->kind) {
+    case TuningKey::kBool: value = value != 0; break;
+    case TuningKey::kXcds: value = std::max<int32_t>(1, value); break;
+    case TuningKey::kWaves:
+      if (value != 0 && value != 4 && value != 8)
+        return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: prefill_waves must be 0, 4 or 8");
+      break;
+    case TuningKey::kGroup:
+      if (value != 1 && value != 2 && value != 4 && value != 8)
+        return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: decode_group must be 1, 2, 4 or 8");
+      break;
+    case TuningKey::kCount: break;
   }
+  g_tuning.*(k->field) = value;
+  return CB_OK;
+}
+
+extern "C" int cb_get_tuning(const char* key, int32_t* value) {
+  const TuningKey* k = find_tuning_key(key);
+  if (!k) return fail(CB_ERR_INVALID_ARG, "cb_get_tuning: unknown key '%s'", key ? key : "(null)");
+  if (!value) return fail(CB_ERR_INVALID_ARG, "cb_get_tuning: value is NULL");
+  *value = g_tuning.*(k->field);
   return CB_OK;
 }
 

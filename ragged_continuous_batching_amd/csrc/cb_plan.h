@@ -128,7 +128,6 @@ struct PrefillArgs {
   int32_t n_items;
   int32_t num_q_heads, num_kv_heads, max_blocks, num_blocks;
   float scale_log2;
-  int32_t touch_ahead;    // 1: pull the key tile two steps ahead toward L2
   const StepDesc* desc;   // non-null in a replayed step: sizes and arrays come from here
   float* part_o;          // partial outputs of split items, as RowArgs::part_o / part_ml
   float* part_ml;

@@ -41,7 +41,7 @@ struct cb_graph {
   // what the current graphs were captured for
   bool captured = false;
   size_t cap_stage = 0, ws_bytes = 0;
-  int prefill_waves = 0, group = 1, touch = 0;
+  int prefill_waves = 0, group = 1;
   bool mfma_decode = false;
   void* ws = nullptr;                       // device workspace, owned
   struct Slot {                             // pinned staging buffer and the graph that reads it
@@ -153,7 +153,6 @@ int graph_capture(cb_graph* g, const Plan& p, const GraphLayout& l) {
   g->prefill_waves = p.prefill_waves;
   g->mfma_decode = p.mfma_decode;
   g->group = p.group;
-  g->touch = g_tuning.prefill_touch;
 
   const cb_shape* sh = &g->shape;
   const int eb = elem_bytes(sh);
@@ -195,7 +194,7 @@ int graph_capture(cb_graph* g, const Plan& p, const GraphLayout& l) {
     if (e == hipSuccess) e = launch_kv_append(aa, eb, sh->head_dim, cs);
     if (e == hipSuccess && prefill) {
       PrefillArgs pa{g->q, g->k_cache, g->v_cache, g->o, nullptr, nullptr, nullptr, nullptr, 1,
-                     sh->num_q_heads, sh->num_kv_heads, 0, sh->num_blocks, scale_log2, g->touch, desc};
+                     sh->num_q_heads, sh->num_kv_heads, 0, sh->num_blocks, scale_log2, desc};
       e = launch_prefill(pa, sh->head_dim, g->prefill_waves, cs);
     }
     if (e == hipSuccess) {
@@ -308,7 +307,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0, false, slots ? bt_rows.data() : nullptr);
   const GraphLayout l = graph_layout(num_reqs, nbt, num_tokens, p);
   const bool fits = g->captured && l.stage_bytes <= g->cap_stage && l.total <= g->ws_bytes &&
-                    p.mfma_decode == g->mfma_decode && p.group == g->group && g_tuning.prefill_touch == g->touch;
+                    p.mfma_decode == g->mfma_decode && p.group == g->group;
   if (!fits && (st = graph_capture(g, p, l))) return st;
 
   cb_graph::Slot& sl = g->slot[g->next];

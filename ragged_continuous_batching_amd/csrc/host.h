@@ -36,7 +36,6 @@ struct Tuning {
   int32_t target_waves = 0;       // 0: 8192 wave items (vector-ALU decode), 4096 (matrix-core decode)
   int32_t overlap_prefill = 0;    // 1 = run prefill tiles on a side stream beside decode rows
   int32_t xcds = 8;               // XCDs that work-groups are dispatched over (MI355X: 8)
-  int32_t prefill_touch = 0;      // 1: prefill pulls key tiles two steps ahead toward L2
   int32_t decode_group = 8;       // most query heads one decode wave handles (1, 2, 4 or 8)
   int32_t decode_mfma = 1;        // 1: grouped-query decode (4+ heads per kv head) on MFMA
   int32_t stage_kernel = 1;       // 1: uploads run as a copy kernel on the stream; 0: copy engine

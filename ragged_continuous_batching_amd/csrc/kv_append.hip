@@ -1,8 +1,8 @@
 // KV append: scatter this step's new keys and values into the paged cache.
 //
-// zhangchitc "continuous-batching", section "Inside the kernel": after the QKV projection
-// the new keys and values are written into the KV cache, each into its own request's entry,
-// before attention reads the cache back. The cache is paged (fixed-size physical blocks,
+// zhangchitc "continuous-batching", section "Inside the kernel": once the QKV projection
+// has produced a step's keys and values, each row is stored in the cache slot of the
+// request it belongs to, and only then does attention read the cache. The cache is paged (fixed-size physical blocks,
 // hassanahmed "How continuous batching speeds up LLM serving", paged-memory section).
 //
 // Layout (include/cb.h): K pages are [block_size][D], V pages are [D][block_size] (V is

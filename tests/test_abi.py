@@ -119,12 +119,49 @@ def test_empty_batch_is_a_no_op():
     assert cb.cb_ragged_attention_workspace_size(shape, b) == 0
 
 
+def header_tuning_keys():
+    """The keys listed in cb.h's cb_set_tuning comment, with their documented defaults."""
+    text = open(HEADER).read()
+    block = text[text.index("Tuning knobs"):text.index("int cb_set_tuning")]
+    return re.findall(r'^\s*\*\s+"([a-z_]+)"', block, flags=re.M)
+
+
+TUNING_DEFAULTS = {"split_blocks": 0, "target_waves": 0, "overlap_prefill": 0, "xcds": 8, "decode_mfma": 1,
+                   "decode_group": 8, "stage_kernel": 1, "prefill_waves": 0, "prefill_snake": 1, "prefill_split": 1,
+                   "prefill_split_tiles": 0, "decode_order": 1, "mixed_launch": 0, "mixed_order": 0}
+
+
 def test_tuning_keys():
-    cb.cb_set_tuning("split_blocks", 0)
-    with pytest.raises(cb.CbError):
-        cb.cb_set_tuning("no_such_key", 1)
+    keys = header_tuning_keys()
+    assert sorted(keys) == sorted(TUNING_DEFAULTS), keys
+    for k in keys:
+        assert cb.cb_get_tuning(k) == TUNING_DEFAULTS[k], k
+        with cb.tuned(**{k: 1 if k not in ("prefill_waves", "decode_group") else 4}):
+            assert cb.cb_get_tuning(k) in (1, 4)
+        assert cb.cb_get_tuning(k) == TUNING_DEFAULTS[k], k
+    for bad in ("no_such_key", "prefill_touch"):
+        with pytest.raises(cb.CbError):
+            cb.cb_set_tuning(bad, 1)
+        with pytest.raises(cb.CbError):
+            cb.cb_get_tuning(bad)
     with pytest.raises(cb.CbError):
         cb.cb_set_tuning("split_blocks", -1)
+    for k, v in (("prefill_waves", 6), ("decode_group", 3)):
+        with pytest.raises(cb.CbError):
+            cb.cb_set_tuning(k, v)
+        assert cb.cb_get_tuning(k) == TUNING_DEFAULTS[k]
+    assert cb.lib.cb_get_tuning(b"xcds", None) == cb.CB_ERR_INVALID_ARG
+
+
+def test_every_tuning_key_has_a_gpu_test():
+    """Each documented key is set to a non-default value by some GPU parity test."""
+    tdir = os.path.dirname(os.path.abspath(__file__))
+    text = ""
+    for name in sorted(os.listdir(tdir)):
+        if name.startswith("test_gpu") and name.endswith(".py"):
+            text += open(os.path.join(tdir, name)).read()
+    for k in header_tuning_keys():
+        assert re.search(r'(cb_set_tuning\("%s"|\b%s=)' % (k, k), text), f"no GPU test sets {k}"
 
 
 def test_kv_bytes_per_position_matches_pages():

@@ -46,23 +46,51 @@ def oracle_full(wl, step):
     return A.ragged_attention(q, k, v, hk, hv, step.cu_q_lens, step.ctx_lens, wl.scale)
 
 
-def oracle_rows(wl, step, rows):
-    """fp64 oracle of selected packed rows, computed one request at a time."""
-    rows = np.asarray(sorted(set(int(t) for t in rows)))
-    owner = step.token_to_req[rows]
-    out = {}
-    for i in np.unique(owner):
-        sel = rows[owner == i]
-        rid, c, s = int(step.req_ids[i]), int(step.ctx_lens[i]), int(step.cu_q_lens[i])
-        pos = c + (sel - s)
+def oracle_positions(wl, req_ids, positions, workers=None):
+    """fp64 oracle of query rows given as (request id, absolute position) pairs, in the
+    order given. A token's values depend only on its request and position, so all rows of
+    one request (from one step or from several) are one oracle call over that request's
+    keys 0..max position. Requests run on a thread pool (BLAS single-threaded inside) when
+    there are many of them, else one at a time with threaded BLAS."""
+    import concurrent.futures as cf
+    import os
+    from threadpoolctl import threadpool_limits
+    req_ids = np.asarray(req_ids, dtype=np.int64)
+    positions = np.asarray(positions, dtype=np.int64)
+    out = np.zeros((len(req_ids), wl.num_q_heads, wl.head_dim))
+    order = np.argsort(req_ids, kind="stable")
+    bounds = np.flatnonzero(np.diff(req_ids[order])) + 1
+    groups = np.split(order, bounds) if len(order) else []
+    wl.raw_pool(W.KIND_Q)                         # build the pools once, before the threads
+
+    def one(idx):
+        rid, pos = int(req_ids[idx[0]]), positions[idx]
         L = int(pos.max()) + 1
         keys = wl.values(W.KIND_K, rid, np.arange(L))
         vals = wl.values(W.KIND_V, rid, np.arange(L))
-        q = wl.values(W.KIND_Q, rid, pos)
-        ref = A.attend(q, keys, vals, pos, wl.scale)
-        for t, r in zip(sel, ref):
-            out[int(t)] = r
-    return rows, np.stack([out[int(t)] for t in rows])
+        out[idx] = A.attend(wl.values(W.KIND_Q, rid, pos), keys, vals, pos, wl.scale)
+
+    n = workers or min(16, len(os.sched_getaffinity(0)))
+    if len(groups) >= 4 * n:
+        with threadpool_limits(1), cf.ThreadPoolExecutor(n) as ex:
+            list(ex.map(one, groups))
+    else:
+        for g in groups:
+            one(g)
+    return out
+
+
+def step_positions(step, rows):
+    rows = np.asarray(rows, dtype=np.int64)
+    owner = step.token_to_req[rows]
+    return step.req_ids[owner].astype(np.int64), step.ctx_lens[owner] + (rows - step.cu_q_lens[owner])
+
+
+def oracle_rows(wl, step, rows):
+    """fp64 oracle of selected packed rows of one step (sorted, duplicates dropped)."""
+    rows = np.asarray(sorted(set(int(t) for t in rows)), dtype=np.int64)
+    rids, pos = step_positions(step, rows)
+    return rows, oracle_positions(wl, rids, pos)
 
 
 def run_one_step(wl, **kw):
@@ -305,34 +333,55 @@ def test_config2_mixed_step(reading):
 
 
 def test_config3_decode_gqa():
+    """Every row of the decode-only step (256 requests, lognormal contexts up to 32k)."""
     wl = W.config(3)
     run, step, batch, o = run_one_step(wl)
-    ctx = step.ctx_lens
-    rng = np.random.default_rng(1)
-    rows = sorted(set(np.argsort(ctx)[-8:].tolist()) | set(rng.integers(0, step.num_tokens, 40).tolist()))
-    rows, ref = oracle_rows(wl, step, rows)
-    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 3")
+    rows, ref = oracle_rows(wl, step, range(step.num_tokens))
+    assert len(rows) == 256
+    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 3 (all rows)")
+
+
+def chunk_edge_rows(step, tile=256, boundary=128):
+    """Every row of each prefill chunk's first and last `tile` rows, and the two rows on each
+    side of every multiple of `boundary` inside the chunk (work-group and key-tile edges)."""
+    rows = set()
+    for i in range(step.num_reqs):
+        s, e = int(step.cu_q_lens[i]), int(step.cu_q_lens[i + 1])
+        rows |= set(range(s, min(e, s + tile))) | set(range(max(s, e - tile), e))
+        for b in range(boundary, e - s, boundary):
+            rows |= {s + b - 1, s + b}
+    return sorted(rows)
 
 
 def test_config4_chunked_prefill():
     wl = W.config(4)
     run, step, batch, o = run_one_step(wl)
-    rows, ref = oracle_rows(wl, step, sample_rows(step, 20, np.random.default_rng(2)))
-    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 4")
+    rows, ref = oracle_rows(wl, step, chunk_edge_rows(step))
+    assert len(rows) == 4 * 512 + 4 * 2 * 12
+    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 4 (chunk edges)")
 
 
 def test_config5_trace_replay():
-    """500 steps of the scheduler trace with append + attention every step; sampled rows
-    of every 50th step against the oracle (token values depend only on (request, position),
-    so each request's history is regenerated for the check)."""
+    """500 steps of the scheduler trace with append + attention every step. The first and the
+    last row of every request in the contiguous window of steps 150..199 (about 30k rows;
+    a token's values depend only on its request and position, so each request's rows from
+    all 50 steps are one oracle call), plus sampled rows of every 50th step."""
     wl = W.config(5)
     run = DeviceRun(wl, stale=None)
     rng = np.random.default_rng(5)
     checked = 0
+    win_rid, win_pos, win_got, win_step = [], [], [], []
     for k in range(wl.steps):
         for r in wl.arrivals[k]:
             run.sched.add(r.req_id, r.prompt_len, r.out_len)
         step, batch, q, kn, vn, o = run.run_step()
+        if 150 <= k < 200:
+            rows = np.array(sorted(set(step.cu_q_lens[:-1].tolist()) | set((step.cu_q_lens[1:] - 1).tolist())))
+            rid, pos = step_positions(step, rows)
+            win_rid.append(rid)
+            win_pos.append(pos)
+            win_got.append(o[torch.from_numpy(rows).cuda()].float().cpu())
+            win_step.append(np.full(len(rows), k))
         if k % 50 == 49 or k == 0:
             torch.cuda.synchronize()
             cand = sample_rows(step, 2, rng)
@@ -341,6 +390,10 @@ def test_config5_trace_replay():
             checked += 1
         run.sched.commit()
     assert checked == 11
+    ref = oracle_positions(wl, np.concatenate(win_rid), np.concatenate(win_pos))
+    got = torch.cat(win_got)
+    assert len(got) > 20000
+    check(got, ref, "bf16", "config 5 steps 150-199, first and last row of every request")
 
 
 @pytest.mark.parametrize("batch_size", [1, 3])

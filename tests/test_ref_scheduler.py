@@ -211,8 +211,9 @@ def run_to_completion(s, eos_at=None, max_steps=100000):
 
 
 def test_static_batch_pads_to_longest_and_finishes_together():
-    """zhangchitc "continuous-batching", "Naive batching": A, B and C arrive together, are
-    padded to the longest and keep computing until every one of them has finished."""
+    """zhangchitc "continuous-batching", "Naive batching": requests that start together
+    are padded to the longest prompt, and the batch occupies its rows until its last
+    member is done."""
     s = RefScheduler(token_budget=4, block_size=4, num_blocks=64)
     s.set_static(3)
     for rid, (p, o) in enumerate([(5, 2), (2, 4), (3, 3)]):
