@@ -144,6 +144,29 @@ int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch, const void
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Ragged attention that allocates nothing, for callers that cannot allocate memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results as cb_ragged_attention (bit for bit), without the
+ * workspace: the launch plan and the fp32 split-K partials live in a fixed device array of
+ * CB_NOALLOC_SCRATCH_BYTES that the library keeps on every GPU it runs on until the process
+ * ends (each GPU holds its own copy). The plan is copied into the array on `stream` from
+ * ordinary host memory. The call allocates no device memory and no pinned host memory and
+ * frees nothing (its host-side planning uses the C++ heap).
+ * A batch whose workspace (cb_ragged_attention_workspace_size) is larger than the array is
+ * rejected with CB_ERR_WORKSPACE_TOO_SMALL before anything is copied or launched. Nothing in
+ * the array needs to start at zero: each partial is written before the combine pass reads
+ * it, and a call keeps whatever the previous call left there.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU (on
+ * different streams, or on different threads without ordering between them) race and give
+ * wrong results. Calls on one stream are ordered. The "overlap_prefill" knob does not apply
+ * here (prefill tiles run on `stream`).
+ * ------------------------------------------------------------------------------------- */
+#define CB_NOALLOC_SCRATCH_BYTES (32u << 20)
+int cb_ragged_attention_noalloc(const cb_shape* shape, const cb_batch* batch, const void* q,
+                                const void* k_cache, const void* v_cache, float scale, void* o,
+                                void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * One whole step from host metadata: KV append then ragged attention, with the metadata and
  * the launch plan sent to the device in a single copy. This is the same work as uploading
  * cu_q_lens / ctx_lens / block_tables, calling cb_kv_append and then cb_ragged_attention,

@@ -80,6 +80,8 @@ def _load():
                                             ctypes.POINTER(cb_plan_info)]),
         "cb_ragged_attention": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), P, P, P,
                                                ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "cb_ragged_attention_noalloc": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.POINTER(cb_batch), P, P, P,
+                                                       ctypes.c_float, P, P]),
         "cb_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, P, P]),
         "cb_step_forward": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -123,6 +125,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_plan_describe", "cb_ragged_attention",
+            "cb_ragged_attention_noalloc",
             "cb_step_workspace_size",
             "cb_step_forward", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_get_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
@@ -183,6 +186,16 @@ def cb_ragged_attention(shape: cb_shape, batch: cb_batch, q, k_cache, v_cache, s
     return _check(lib.cb_ragged_attention(ctypes.byref(shape), ctypes.byref(batch), _ptr(q), _ptr(k_cache),
                                           _ptr(v_cache), ctypes.c_float(scale), _ptr(o), _ptr(workspace),
                                           ctypes.c_size_t(workspace_bytes), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20        # CB_NOALLOC_SCRATCH_BYTES in cb.h
+
+
+def cb_ragged_attention_noalloc(shape: cb_shape, batch: cb_batch, q, k_cache, v_cache, scale: float, o,
+                                stream=None) -> int:
+    """cb_ragged_attention without a workspace (the library's fixed device array)."""
+    return _check(lib.cb_ragged_attention_noalloc(ctypes.byref(shape), ctypes.byref(batch), _ptr(q), _ptr(k_cache),
+                                                  _ptr(v_cache), float(scale), _ptr(o), _stream(stream)))
 
 
 def _host_i32(a):

@@ -163,10 +163,13 @@ int side_stream(SideStream** out) {
   return CB_OK;
 }
 
+}  // namespace
+
 // Launches the attention kernels of plan `p`, whose work lists are already in the workspace
 // at `ws` (plan offsets are relative to `ws`). `batch` holds device metadata pointers.
 int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p, char* ws, const void* q,
-                     const void* k_cache, const void* v_cache, float scale, void* o, hipStream_t s) {
+                     const void* k_cache, const void* v_cache, float scale, void* o, hipStream_t s,
+                     bool allow_side_stream) {
   const int eb = elem_bytes(shape);
   const float scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
   hipError_t e = hipSuccess;
@@ -178,7 +181,8 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
   // more than the overlap saved.
   hipStream_t ps = s;
   SideStream* side = nullptr;
-  const bool fork = g_tuning.overlap_prefill && !p.mixed && !p.prefill.empty() && !p.splits.empty();
+  const bool fork =
+      allow_side_stream && g_tuning.overlap_prefill && !p.mixed && !p.prefill.empty() && !p.splits.empty();
   if (fork) {
     if ((st = side_stream(&side))) return st;
     ps = side->stream;
@@ -230,7 +234,6 @@ int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p
   return CB_OK;
 }
 
-}  // namespace
 }  // namespace cb
 
 using namespace cb;
@@ -452,7 +455,7 @@ extern "C" int cb_ragged_attention(const cb_shape* shape, const cb_batch* batch,
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if ((st = upload(ws, p.plan_bytes, s, [&](char* host) { write_plan(p, host); }))) return st;
-  return launch_attention(shape, batch, p, ws, q, k_cache, v_cache, scale, o, s);
+  return launch_attention(shape, batch, p, ws, q, k_cache, v_cache, scale, o, s, true);
 }
 
 extern "C" size_t cb_step_workspace_size(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
@@ -543,7 +546,7 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
     e = launch_kv_append(aa, eb, shape->head_dim, s);
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_step_forward: append launch failed: %s", hipGetErrorString(e));
-  return launch_attention(shape, &b, p, ws + l.plan_base, q, k_cache, v_cache, scale, o, s);
+  return launch_attention(shape, &b, p, ws + l.plan_base, q, k_cache, v_cache, scale, o, s, true);
 }
 
 extern "C" int cb_linear(int32_t M, int32_t N, int32_t K, const void* a, const void* w, void* c, void* stream) {

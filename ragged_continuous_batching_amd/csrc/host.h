@@ -93,6 +93,13 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves = 
                const int32_t* bt_rows = nullptr);
 // Serialises the plan's work lists at their offsets into `out` (plan_bytes long).
 void write_plan(const Plan& p, char* out);
+// Launches the attention kernels of plan `p` on stream `s`; its work lists are already at
+// `ws` (device), and its partials go to `ws` + the plan's partial offsets. With
+// allow_side_stream and the "overlap_prefill" knob, the prefill kernel runs on the library's
+// side stream (created on first use) and is joined back before the combine pass.
+int launch_attention(const cb_shape* shape, const cb_batch* batch, const Plan& p, char* ws, const void* q,
+                     const void* k_cache, const void* v_cache, float scale, void* o, hipStream_t s,
+                     bool allow_side_stream);
 
 // ---- step layouts (plan.cpp) ---------------------------------------------------------------
 // Workspace layout of cb_step_forward: the step metadata (cu_q_lens, ctx_lens, the block

@@ -253,3 +253,19 @@ def test_graph_entry_points_check_arguments():
         cb.CB_ERR_INVALID_ARG
     assert cb.lib.cb_graph_stats(None, None, None, None) == cb.CB_ERR_INVALID_ARG
     cb.lib.cb_graph_destroy(None)
+
+
+def test_noalloc_rejects_a_plan_larger_than_its_array():
+    """cb_ragged_attention_noalloc checks the batch's workspace against its fixed array before
+    it touches the device: a 256-row chunk after 16k cached tokens split into one-tile key
+    ranges needs about 1 GiB of partials."""
+    shape = cb.make_shape(32, 32, 128, 4096, "bf16")
+    b = _batch([0, 256], [16384], 1040)
+    with cb.tuned(prefill_split_tiles=1):
+        need = cb.cb_ragged_attention_workspace_size(shape, b)
+        assert need > cb.NOALLOC_SCRATCH_BYTES
+        st = cb.lib.cb_ragged_attention_noalloc(ctypes.byref(shape), ctypes.byref(b), FAKE, FAKE, FAKE, 0.1, FAKE,
+                                                None)
+    assert st == cb.CB_ERR_WORKSPACE_TOO_SMALL
+    assert "fixed" in cb.cb_last_error()
+    assert "CB_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
