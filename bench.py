@@ -82,17 +82,24 @@ def measured_traffic(kernel, workload):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, step, budget_s=25.0):
-    """Times the fp64 oracle on this step's rows (all of them if they fit the budget,
-    else the largest prefix of requests in a fixed order that does)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def _oracle_sample(wl, step, budget_s):
+    """(rows done, requests done, seconds): the fp64 oracle over the step's requests in
+    packed order, one call per request including the gathering of its inputs, until the
+    budget is spent."""
     import numpy as np
     import workloads as W
     from oracle import attention as A
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
     t_start = time.perf_counter()
     done_tokens, done_reqs = 0, 0
     for i in range(step.num_reqs):
@@ -107,11 +114,28 @@ def cpu_baseline(wl, step, budget_s=25.0):
         done_reqs += 1
         if time.perf_counter() - t_start > budget_s:
             break
-    dt = time.perf_counter() - t_start
-    sample = (f"all {step.num_reqs} requests ({step.num_tokens} rows) of the step" if done_reqs == step.num_reqs
-              else f"first {done_reqs} of {step.num_reqs} requests ({done_tokens} of {step.num_tokens} rows)")
-    return {"value": done_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": sample + ", fp64 numpy, one call per request incl. gathering inputs", "seconds": round(dt, 3)}
+    return done_tokens, done_reqs, time.perf_counter() - t_start
+
+
+def cpu_baseline(wl, step, budget_s=25.0, one_thread_budget_s=15.0):
+    """Times the fp64 oracle on this step's rows (all of them if they fit the budget, else
+    the largest prefix of requests in packed order that does), once with the BLAS threads
+    numpy has (all host cores the process may use) and once on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    wl.raw_pool(0)                               # the value pools are built before timing
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+
+    def sample_text(tokens, reqs):
+        return (f"all {step.num_reqs} requests ({step.num_tokens} rows) of the step" if reqs == step.num_reqs
+                else f"first {reqs} of {step.num_reqs} requests ({tokens} of {step.num_tokens} rows)")
+    tokens, reqs, dt = _oracle_sample(wl, step, budget_s)
+    with threadpool_limits(1):
+        tokens1, reqs1, dt1 = _oracle_sample(wl, step, one_thread_budget_s)
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample_text(tokens, reqs) + ", fp64 numpy, one call per request incl. gathering inputs",
+            "seconds": round(dt, 3), "cpu_model": cpu_model(), "host_cores_visible": len(os.sched_getaffinity(0)),
+            "one_thread": {"value": round(tokens1 / dt1, 1), "unit": "tokens/s", "cores": 1,
+                           "sample": sample_text(tokens1, reqs1), "seconds": round(dt1, 3)}}
 
 
 def launch_step(cb, run, st, q, k_new, v_new, o, ws, stream):
@@ -127,9 +151,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5],
-                    help="2: mixed step (default), 3: decode-only GQA, 4: chunked prefill, "
-                         "5: the 500-step scheduler trace (steps = trace steps after the warm-up)")
+    ap.add_argument("--config", type=int, default=None, choices=[2, 3, 4, 5],
+                    help="one workload only: 2 mixed step, 3 decode-only GQA, 4 chunked prefill, 5 the 500-step "
+                         "scheduler trace (steps = trace steps after the warm-up). Default: config 2 is the "
+                         "headline and configs 3, 4 and 5 are reported under 'configs' in the same line")
+    ap.add_argument("--no-subconfigs", action="store_true",
+                    help="default run: report config 2 only (no 'configs' sub-results)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--api", choices=["fused", "split"], default="fused",
                     help="fused: one cb_step_forward call per step (one metadata upload); split: Batch upload + "
@@ -174,12 +201,9 @@ def main(argv=None):
               "the multi-GPU design is described but not built.", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    import workloads as W
     from ragged_continuous_batching_amd import cb
-    from ragged_continuous_batching_amd.runner import DeviceRun
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     for kv in args.tune:
@@ -189,8 +213,6 @@ def main(argv=None):
         return bench_policies(args)
     if args.layer:
         return bench_layer(args)
-    if args.config == 5:
-        return bench_trace(args)
     if args.copy_calibration:
         src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -198,17 +220,60 @@ def main(argv=None):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.config == 5:
+        result = bench_trace(args)
+    elif args.config is not None or args.long_chunk:
+        result = bench_fixed(args, args.config or 0)
+    else:
+        result = bench_fixed(args, 2)
+        if not args.no_subconfigs:
+            result["configs"] = {}
+            for c in (3, 4):
+                release_device_memory()
+                result["configs"][str(c)] = sub_result(bench_fixed(args, c, cpu_budget_s=5.0))
+            release_device_memory()
+            result["configs"]["5"] = sub_result(bench_trace(args, trace_window=True))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def release_device_memory():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+SUB_KEYS = ("config", "steps", "warmup", "ms_per_step", "value", "unit", "device_ms_per_step", "roofline",
+            "kernels", "cpu_baseline", "window")
+
+
+def sub_result(r):
+    """The fields of another workload's result that go into the headline line."""
+    return {k: r[k] for k in SUB_KEYS if k in r}
+
+
+def bench_fixed(args, cfg, cpu_budget_s=25.0):
+    """One fixed step (configs 2-4, or the late chunk when cfg = 0), rebuilt from the same
+    scheduler state every step. Returns the result dict."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from ragged_continuous_batching_amd import cb
+    from ragged_continuous_batching_amd.runner import DeviceRun
+
     names = {2: "llama2-7b-shaped mixed step (64 decodes + 2x992 prefill chunks)",
              3: "decode-only GQA (256 decodes, lognormal contexts)",
              4: "chunked-prefill-heavy (4x2048-token chunks)"}
-    if args.long_chunk:
+    if cfg == 0:
         n = args.long_chunk
         wl = W.custom([W.Request(0, n + 256, 1 << 20, cached=n, generated=0)], num_q_heads=32, num_kv_heads=32,
                       head_dim=128, dtype="bf16", seed=1006, token_budget=256)
-        args.config = 0
         names[0] = f"late chunk of a long prompt (256 rows after {n} cached tokens, Hq=Hkv=32, D=128)"
     else:
-        wl = W.config(args.config)
+        wl = W.config(cfg)
     run = DeviceRun(wl, stale=None)
     base = run.sched
     # setup: write the cached history once (not timed)
@@ -266,7 +331,7 @@ def main(argv=None):
         if n:
             kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "timed_steps": False}
     cb.cb_profile_reset()
-    dominant = "prefill" if args.config in (0, 4) else "decode"
+    dominant = "prefill" if cfg in (0, 4) else "decode"
     if dominant == "decode" and "mixed" in kernels:
         dominant = "mixed"                 # prefill tiles and decode waves in one launch
 
@@ -311,7 +376,7 @@ def main(argv=None):
     roof["kernel"] = cb.cb_kernel_name(cb.KERNELS[dominant])
     if dominant == "decode" and wl.dtype == "bf16" and wl.num_q_heads // wl.num_kv_heads >= 4:
         roof["kernel"] = "row_attn_mfma_kernel"        # grouped-query decode runs on the matrix cores
-    roof["traffic"] = measured_traffic(roof["kernel"], f"config{args.config}")
+    roof["traffic"] = measured_traffic(roof["kernel"], f"config{cfg}")
 
     result = {
         "metric": "ragged-attention tokens/s per step",
@@ -326,7 +391,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": names[args.config], "num_tokens": T, "num_reqs": step0.num_reqs,
+        "config": {"workload": names[cfg], "num_tokens": T, "num_reqs": step0.num_reqs,
                    "num_decode": step0.num_decode, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "token_budget": wl.token_budget,
                    "seed": wl.seed, "api": args.api},
@@ -345,9 +410,10 @@ def main(argv=None):
         result.update(bench_graph_step(args, cb, run, base, q, k_new, v_new, o, stream))
         result["config"]["api"] = "graph"
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, step0)
-    print(json.dumps(result), flush=True)
-    return 0
+        result["cpu_baseline"] = cpu_baseline(wl, step0, budget_s=cpu_budget_s,
+                                              one_thread_budget_s=min(15.0, cpu_budget_s))
+    del run, q, k_new, v_new, o, ws
+    return result
 
 
 def bench_graph_step(args, cb, run, base, q, k_new, v_new, o, stream):
@@ -410,10 +476,15 @@ def bench_graph_step(args, cb, run, base, q, k_new, v_new, o, stream):
                       "roofline_from": "kernel events of the eager pass of this run (same kernels, same plan)"}}
 
 
-def bench_trace(args):
+TRACE_WINDOW_WARMUP = 5          # the trace's timed window as a sub-result: steps 5..499
+
+
+def bench_trace(args, trace_window=False):
     """Scheduler-trace replay (Hq=64, Hkv=8, m=4096, Poisson(8) arrivals, 500 steps): every
     step is built by the step builder, appended and attended. Step inputs come from fixed
-    synthetic Q/K/V buffers of m rows resident in HBM (values do not change the work)."""
+    synthetic Q/K/V buffers of m rows resident in HBM (values do not change the work).
+    trace_window: time steps 5..499 whatever --steps/--warmup say (the sub-result of the
+    default run). Returns the result dict."""
     import numpy as np
     import torch
 
@@ -423,8 +494,12 @@ def bench_trace(args):
 
     wl = W.config(5)
     total_steps = wl.steps
-    warm = min(args.warmup, total_steps - 1)
-    steps = min(args.steps if args.steps != 50 else total_steps - warm, total_steps - warm)
+    if trace_window:
+        warm, steps = TRACE_WINDOW_WARMUP, total_steps - TRACE_WINDOW_WARMUP
+    else:
+        warm = min(args.warmup, total_steps - 1)
+        steps = min(args.steps if args.steps != 50 else total_steps - warm, total_steps - warm)
+    cpu_step_index = warm + steps // 2          # the oracle is timed on this step's batch
     sched = None
     if args.pool_blocks:
         sched = cb.Scheduler(wl.token_budget, wl.block_size, args.pool_blocks, wl.max_num_seqs)
@@ -454,6 +529,8 @@ def bench_trace(args):
         alg_pre_bytes.append(alg["prefill"]["bytes"])
         both.append(alg["decode"]["tokens"] > 0 and alg["prefill"]["tokens"] > 0)
         tokens.append(st.num_tokens)
+        if kstep == cpu_step_index:
+            cpu_step = st
         dry.commit()
     del dry
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
@@ -574,11 +651,17 @@ def bench_trace(args):
         "device_ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
         "kernels": kernels,
     }
+    result["window"] = f"trace steps {warm}..{warm + steps - 1} timed (steps 0..{warm - 1} warm up)"
+    if roofline is not None:
+        roofline["traffic"] = measured_traffic(roofline["kernel"], f"config5_steps{warm}-{warm + steps - 1}")
     if graph_stats is not None:
         result["graph"] = {"buckets": graph_stats,
                            "roofline": "null: kernels inside a graph carry no per-kernel events"}
-    print(json.dumps(result), flush=True)
-    return 0
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, cpu_step, budget_s=5.0, one_thread_budget_s=5.0)
+        result["cpu_baseline"]["sample"] += f" (trace step {cpu_step_index})"
+    del run, q, k_new, v_new, o, ws
+    return result
 
 
 def bench_layer(args):
