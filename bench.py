@@ -246,7 +246,7 @@ def release_device_memory():
 
 
 SUB_KEYS = ("config", "steps", "warmup", "ms_per_step", "value", "unit", "device_ms_per_step", "roofline",
-            "kernels", "cpu_baseline", "window")
+            "kernels", "cpu_baseline", "window", "kernels_all", "prefill_roofline")
 
 
 def sub_result(r):
@@ -513,7 +513,7 @@ def bench_trace(args, trace_window=False):
     o = torch.empty_like(q)
     # dry run of the schedule on a copy: the largest workspace any step needs
     dry = run.sched.clone()
-    need, alg_dec_bytes, alg_pre_bytes, both, tokens, preempted = 0, [], [], [], [], []
+    need, alg_dec_bytes, alg_pre_bytes, both, tokens, preempted, alg_pre_flops = 0, [], [], [], [], [], []
     for kstep in range(total_steps):
         for r in wl.arrivals[kstep]:
             dry.add(r.req_id, r.prompt_len, r.out_len)
@@ -527,6 +527,7 @@ def bench_trace(args, trace_window=False):
         alg = algorithmic(wl, st)
         alg_dec_bytes.append(alg["decode"]["bytes"])
         alg_pre_bytes.append(alg["prefill"]["bytes"])
+        alg_pre_flops.append(alg["prefill"]["flops"])
         both.append(alg["decode"]["tokens"] > 0 and alg["prefill"]["tokens"] > 0)
         tokens.append(st.num_tokens)
         if kstep == cpu_step_index:
@@ -541,7 +542,7 @@ def bench_trace(args, trace_window=False):
         from ragged_continuous_batching_amd.runner import GraphSteps
         gs = GraphSteps(run, q, k_new, v_new, o, min_bucket=256)
 
-    def one(kstep):
+    def one(kstep, sched=sched):
         for r in wl.arrivals[kstep]:
             sched.add(r.req_id, r.prompt_len, r.out_len)
         if gs is not None:
@@ -568,6 +569,9 @@ def bench_trace(args, trace_window=False):
     for kstep in range(warm):
         one(kstep)
     torch.cuda.synchronize()
+    # the scheduler state at the start of the window, for a second (profiled) pass over it
+    profile_pass = not (args.no_kernel_events or args.all_kernel_events or gs is not None or args.api != "fused")
+    window_start = sched.clone() if profile_pass else None
     cb.cb_profile_reset()
     # Only the launches that stream the cache carry events in the timed steps (each event
     # pair costs the stream about a microsecond or two), unless every kernel is asked for.
@@ -614,6 +618,30 @@ def bench_trace(args, trace_window=False):
                     "share_of_steps_at_or_above_0.70": round(float((eff >= 0.70).mean()), 4),
                     "steps": int(len(eff))}
     cb.cb_profile_reset()
+    if profile_pass:
+        # The same window again from the same scheduler state, with an event pair around every
+        # kernel (not part of the timed rate): each kernel's share of the step and the prefill
+        # kernel's MFMA fraction over the window.
+        cb.cb_profile_select(None)
+        cb.cb_profile_enable(True)
+        for kstep in range(warm, warm + steps):
+            one(kstep, window_start)
+        torch.cuda.synchronize()
+        cb.cb_profile_enable(False)
+        all_kernels = {}
+        for name, kid in cb.KERNELS.items():
+            ms, n = cb.cb_profile_read(kid)
+            if n:
+                all_kernels[name] = {"avg_us": round(ms * 1e3 / n, 2), "launches": n, "total_ms": round(ms, 3)}
+        cb.cb_profile_reset()
+    else:
+        all_kernels = kernels if args.all_kernel_events else None
+    prefill_roof = None
+    if all_kernels and "prefill" in all_kernels:
+        pre_tflops = sum(alg_pre_flops[warm:warm + steps]) / (all_kernels["prefill"]["total_ms"] * 1e-3) / 1e12
+        prefill_roof = {"bound": "mfma", "achieved": round(pre_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4), "kernel": "prefill_kernel",
+                        "flops_over_window": int(sum(alg_pre_flops[warm:warm + steps]))}
     T_total = int(sum(tokens[warm:warm + steps]))
     dec_bytes = int(sum(alg_dec_bytes[warm:warm + steps]))
     graph_stats = None
@@ -652,6 +680,12 @@ def bench_trace(args, trace_window=False):
         "kernels": kernels,
     }
     result["window"] = f"trace steps {warm}..{warm + steps - 1} timed (steps 0..{warm - 1} warm up)"
+    if all_kernels is not None and profile_pass:
+        result["kernels_all"] = all_kernels
+        result["kernels_all_note"] = ("a second pass over the same window with an event pair around every "
+                                      "kernel (not timed for the rate)")
+    if prefill_roof is not None:
+        result["prefill_roofline"] = prefill_roof
     if roofline is not None:
         roofline["traffic"] = measured_traffic(roofline["kernel"], f"config5_steps{warm}-{warm + steps - 1}")
     if graph_stats is not None:

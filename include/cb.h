@@ -123,7 +123,7 @@ size_t cb_ragged_attention_workspace_size(const cb_shape* shape, const cb_batch*
  * tests and tools that check the planner's choices; the fields are counts of the launch
  * lists, with the tuning knobs in effect at the call. */
 typedef struct {
-  int32_t prefill_rows;          /* query rows per prefill work-group: 128, 256, or 0 (none) */
+  int32_t prefill_rows;          /* query rows per prefill work-group (32 per wave / heads), 0: none */
   int32_t prefill_items;         /* prefill work-groups, empty launch-order slots included */
   int32_t prefill_split_items;   /* of those, items covering one key range of a split tile */
   int32_t decode_splits;         /* row splits of the split-K path (decode rows; fp32 prefill rows) */
@@ -135,6 +135,7 @@ typedef struct {
   int32_t matrix_core_decode;    /* 1: the split-K rows run on the matrix-core kernel */
   int32_t combine_rows;          /* rows merged by the combine pass */
   int32_t mixed;                 /* 1: prefill tiles and decode waves share one launch */
+  int32_t prefill_heads;         /* query heads per prefill work-group (of one kv head), 0: none */
 } cb_plan_info;
 /* Returns CB_OK, or the error cb_ragged_attention would return for the shape and batch. */
 int cb_plan_describe(const cb_shape* shape, const cb_batch* batch, cb_plan_info* out);
@@ -302,6 +303,10 @@ const char* cb_version(void);
  *                    (Hq/Hkv >= 4) runs its prefill tiles (128-row work-groups) and decode
  *                    waves in one launch, interleaved so that both kinds share every CU;
  *                    0: two launches. Steps taken by cb_graph_step always use two launches.
+ *   "prefill_heads"  query heads of one kv head that a bf16 prefill work-group takes side
+ *                    by side (1, 2, 4 or 8, capped by the group size and the waves): its
+ *                    waves split into heads x 32-row blocks and share every key/value tile,
+ *                    so a work-group covers 32 x waves / heads rows; 0 (default) = 4
  *   "mixed_order"    order of the mixed launch: 0 (default) spreads prefill and decode
  *                    work-groups in proportion to their counts; 1 alternates them until one
  *                    kind runs out

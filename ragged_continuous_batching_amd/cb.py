@@ -50,7 +50,8 @@ class cb_batch(ctypes.Structure):
 class cb_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "prefill_rows", "prefill_items", "prefill_split_items", "decode_splits", "decode_items", "split_blocks",
-        "split_min_blocks", "split_max_blocks", "longest_first", "matrix_core_decode", "combine_rows", "mixed")]
+        "split_min_blocks", "split_max_blocks", "longest_first", "matrix_core_decode", "combine_rows", "mixed",
+        "prefill_heads")]
 
 
 class cb_step(ctypes.Structure):

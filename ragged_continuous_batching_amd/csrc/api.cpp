@@ -249,7 +249,7 @@ namespace {
 struct TuningKey {
   const char* name;
   int32_t Tuning::*field;
-  enum Kind { kCount, kBool, kXcds, kWaves, kGroup } kind;
+  enum Kind { kCount, kBool, kXcds, kWaves, kGroup, kHeads } kind;
 };
 constexpr TuningKey kTuningKeys[] = {
     {"split_blocks", &Tuning::split_blocks, TuningKey::kCount},
@@ -266,6 +266,7 @@ constexpr TuningKey kTuningKeys[] = {
     {"mixed_launch", &Tuning::mixed_launch, TuningKey::kBool},
     {"decode_order", &Tuning::decode_order, TuningKey::kBool},
     {"mixed_order", &Tuning::mixed_order, TuningKey::kBool},
+    {"prefill_heads", &Tuning::prefill_heads, TuningKey::kHeads},
 };
 
 const TuningKey* find_tuning_key(const char* key) {
@@ -291,6 +292,10 @@ extern "C" int cb_set_tuning(const char* key, int32_t value) {
     case TuningKey::kGroup:
       if (value != 1 && value != 2 && value != 4 && value != 8)
         return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: decode_group must be 1, 2, 4 or 8");
+      break;
+    case TuningKey::kHeads:
+      if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)
+        return fail(CB_ERR_INVALID_ARG, "cb_set_tuning: prefill_heads must be 0, 1, 2, 4 or 8");
       break;
     case TuningKey::kCount: break;
   }
@@ -418,7 +423,8 @@ extern "C" int cb_plan_describe(const cb_shape* shape, const cb_batch* batch, cb
   if (batch->num_tokens == 0) return CB_OK;
   Plan p;
   make_plan(shape, batch, p);
-  out->prefill_rows = p.prefill.empty() ? 0 : 32 * p.prefill_waves;
+  out->prefill_rows = p.prefill.empty() ? 0 : (32 * p.prefill_waves) >> p.prefill_heads_log2;
+  out->prefill_heads = p.prefill.empty() ? 0 : 1 << p.prefill_heads_log2;
   out->prefill_items = static_cast<int32_t>(p.prefill.size());
   for (const PrefillItem& it : p.prefill)
     if (it.req >= 0 && it.part_base >= 0) ++out->prefill_split_items;

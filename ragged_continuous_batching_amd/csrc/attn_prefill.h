@@ -7,8 +7,10 @@
 // masked pairs are not computed at all, and the cache is read one block at a time into a
 // running online-softmax state.
 //
-// One work-group (4 or 8 waves) = 128 or 256 query rows of one request and one query head.
-// Each wave owns 32 rows. Keys stream through LDS in tiles of 64 (4 cache blocks),
+// One work-group (4 or 8 waves) = 32 query rows per wave of one request: 128 or 256 rows of
+// one query head, or fewer rows of several query heads that share one kv head (grouped-query
+// attention: the waves then split into heads x row blocks and read the same key/value
+// tiles). Each wave owns 32 rows of one head. Keys stream through LDS in tiles of 64 (4 cache blocks),
 // double-buffered, and the global loads of later tiles overlap the current tile's math.
 // The products are computed transposed so that the query index stays the lane index:
 //   S^T[key][q] = K Q^T      A = K tile rows from LDS, B = the wave's Q rows (registers)
@@ -52,7 +54,7 @@ template <int D, int NW>
 __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   using Geo = PrefillGeom<D>;
   constexpr int NT = 64 * NW;                           // threads
-  constexpr int ROWS = 32 * NW;                         // query rows of the work-group
+  constexpr int ROWS = 32 * NW;                         // row x head pairs of the work-group
   constexpr int KS = Geo::KS, VS = Geo::VS, DCH = Geo::DCH, DT = Geo::DT;
   __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
 
@@ -60,9 +62,11 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   if (slot >= a.n_items) return;                              // past a replayed step's items
   const PrefillItem it = a.items[slot];
   if (it.req < 0) return;                                     // padding slot of the launch order
-  const int r = it.req, h = it.head;
+  const int hl = it.heads_log2;                               // query heads of the work-group
+  const int rows_wg = ROWS >> hl;                             // query rows of the work-group
+  const int r = it.req;
   const int hkv = a.num_kv_heads;
-  const int g = h / (a.num_q_heads / hkv);
+  const int g = it.head / (a.num_q_heads / hkv);
   const int t0 = a.cu_q_lens[r];
   const int nq = a.cu_q_lens[r + 1] - t0;
   const int c = a.ctx_lens[r];
@@ -70,11 +74,12 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int col = lane & 31, grp = lane >> 5;
-  const int wave_row0 = it.q_begin + wave * 32;              // first row of this wave
+  const int h = it.head + (wave & ((1 << hl) - 1));          // this wave's query head
+  const int wave_row0 = it.q_begin + (wave >> hl) * 32;      // first row of this wave
   const int qrow = wave_row0 + col;                           // this lane's row in the request
   const bool wave_active = wave_row0 < nq;
   const int wave_keys = c + min(wave_row0 + 31, nq - 1) + 1;  // keys any row of the wave sees
-  const int wg_keys = c + min(it.q_begin + ROWS - 1, nq - 1) + 1;
+  const int wg_keys = c + min(it.q_begin + rows_wg - 1, nq - 1) + 1;
   const int kt0 = it.kt_begin;                                // absolute first key tile
   const int n_tiles = it.kt_end - kt0;                        // tiles of this item (local 0..)
   const int32_t* bt = a.block_tables + it.bt_row;

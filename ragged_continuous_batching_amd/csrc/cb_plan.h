@@ -28,9 +28,11 @@ struct CombineRow {
   int32_t pad;
 };
 
-// One tile of a prefill chunk: rows q_begin .. q_begin+R-1 of request `req` (R = 32 x the
-// work-group's waves, clipped to its row count), query head `head`, key tiles
-// kt_begin .. kt_end-1 (64 keys each). req < 0 marks an empty slot. part_base < 0: the item
+// One tile of a prefill chunk: rows q_begin .. q_begin+R-1 of request `req` and query heads
+// head .. head + 2^heads_log2 - 1 (all of one kv head), key tiles kt_begin .. kt_end-1 (64
+// keys each). The work-group's waves split into 2^heads_log2 heads x R/32 row blocks of 32,
+// so R = 32 x waves / 2^heads_log2, clipped to the request's rows; every wave reads the same
+// key/value tiles. req < 0 marks an empty slot. part_base < 0: the item
 // walks all of its rows' keys and writes O. Otherwise it is split `split & 0xffff` of
 // `split >> 16` over the key range: row i of the tile writes its unnormalised output and
 // (max, sum) to partial slot part_base + i * (split >> 16) + (split & 0xffff), and the combine
@@ -45,6 +47,7 @@ struct PrefillItem {
   int32_t kt_end;
   int32_t part_base;
   int32_t split;
+  int32_t heads_log2;   // query heads per work-group, log2 (0: one head)
 };
 
 // Header at the start of a captured step's workspace (cb_graph_*). The host writes it into

@@ -48,6 +48,8 @@ struct Tuning {
   int32_t prefill_split_tiles = 0;  // key tiles per split, forcing splits (tests); 0 = automatic
   int32_t mixed_launch = 0;       // 1: prefill tiles and matrix-core decode waves in one launch
   int32_t decode_order = 1;       // 1: decode splits longest first; 0: rows longest first
+  int32_t prefill_heads = 0;      // query heads per bf16 prefill work-group (one kv head's;
+                                  // 0 = automatic)
   int32_t mixed_order = 0;        // 0: merge prefill and decode chunks in proportion to their
                                   // counts; 1: alternate them until one kind runs out
 };
@@ -76,6 +78,7 @@ struct Plan {
   int group = 1;         // query heads per decode wave
   bool mfma_decode = false;  // decode rows on the MFMA kernel
   int prefill_waves = 4;     // waves (x 32 query rows) per prefill work-group
+  int prefill_heads_log2 = 0;  // query heads per prefill work-group (log2); rows = 32 waves / heads
   int n_sub = 1;         // decode waves per kv head
   int32_t split_blocks = 0;  // split length chosen for the split-K rows
   bool mixed = false;    // prefill tiles and decode waves in one launch (order below)

@@ -128,7 +128,8 @@ def header_tuning_keys():
 
 TUNING_DEFAULTS = {"split_blocks": 0, "target_waves": 0, "overlap_prefill": 0, "xcds": 8, "decode_mfma": 1,
                    "decode_group": 8, "stage_kernel": 1, "prefill_waves": 0, "prefill_snake": 1, "prefill_split": 1,
-                   "prefill_split_tiles": 0, "decode_order": 1, "mixed_launch": 0, "mixed_order": 0}
+                   "prefill_split_tiles": 0, "decode_order": 1, "mixed_launch": 0, "mixed_order": 0,
+                   "prefill_heads": 0}
 
 
 def test_tuning_keys():
@@ -136,7 +137,7 @@ def test_tuning_keys():
     assert sorted(keys) == sorted(TUNING_DEFAULTS), keys
     for k in keys:
         assert cb.cb_get_tuning(k) == TUNING_DEFAULTS[k], k
-        with cb.tuned(**{k: 1 if k not in ("prefill_waves", "decode_group") else 4}):
+        with cb.tuned(**{k: 1 if k not in ("prefill_waves", "decode_group", "prefill_heads") else 4}):
             assert cb.cb_get_tuning(k) in (1, 4)
         assert cb.cb_get_tuning(k) == TUNING_DEFAULTS[k], k
     for bad in ("no_such_key", "prefill_touch"):
@@ -146,7 +147,7 @@ def test_tuning_keys():
             cb.cb_get_tuning(bad)
     with pytest.raises(cb.CbError):
         cb.cb_set_tuning("split_blocks", -1)
-    for k, v in (("prefill_waves", 6), ("decode_group", 3)):
+    for k, v in (("prefill_waves", 6), ("decode_group", 3), ("prefill_heads", 3)):
         with pytest.raises(cb.CbError):
             cb.cb_set_tuning(k, v)
         assert cb.cb_get_tuning(k) == TUNING_DEFAULTS[k]

@@ -85,3 +85,46 @@ def test_target_waves_split_sizing(target, hq, hkv):
     with tuned(target_waves=target):
         run, step, batch, o = run_one_step(wl)
     check(o, oracle_full(wl, step), "bf16", f"target_waves={target} Hq={hq} Hkv={hkv}")
+
+
+@pytest.mark.parametrize("heads", [2, 4, 8])
+@pytest.mark.parametrize("name,hq,hkv,d,waves,split_tiles", [
+    ("mixed", 8, 2, 128, 8, 0), ("mixed", 8, 1, 128, 4, 0), ("tile_edges", 16, 2, 128, 8, 0),
+    ("tile_edges", 32, 2, 64, 4, 0), ("late_chunk", 8, 1, 128, 0, 0), ("mixed", 16, 4, 64, 8, 2),
+    ("long_decode", 64, 8, 128, 8, 3), ("mixed", 4, 2, 128, 4, 1)])
+def test_prefill_heads_per_work_group(heads, name, hq, hkv, d, waves, split_tiles):
+    """Several query heads of one kv head per prefill work-group (waves split into heads x
+    32-row blocks over shared key/value tiles), with forced key-range splits in some cases;
+    the heads per work-group are capped by the group size and the waves."""
+    wl = small_workload(name, hq, hkv, d, "bf16")
+    with tuned(prefill_heads=heads, prefill_waves=waves, prefill_split_tiles=split_tiles):
+        run, step, batch, o = run_one_step(wl)
+        desc = cb.cb_plan_describe(cb.make_shape(hq, hkv, d, wl.num_blocks, "bf16"), cb.Batch.from_step(step).struct)
+    assert desc["prefill_heads"] == min(heads, hq // hkv, waves or 8) or waves == 0, desc
+    check(o, oracle_full(wl, step), "bf16", f"prefill_heads={heads} {name} Hq={hq} Hkv={hkv} D={d} w={waves}")
+
+
+@pytest.mark.parametrize("heads", [2, 8])
+def test_prefill_heads_mixed_launch_and_graph(heads):
+    """Shared-kv-head prefill items in the mixed launch (4-wave work-groups) and in a captured
+    step: bit-identical to the two-launch eager step with the same items."""
+    wl = small_workload("mixed", 16, 2, 128, "bf16")
+    with tuned(prefill_heads=heads, prefill_waves=4):
+        _, step, _, base = run_one_step(wl)
+        with tuned(mixed_launch=1):
+            _, _, _, o_mixed = run_one_step(wl)
+        run = DeviceRun(wl)
+        st = run.sched.build()
+        run.write_history(st)
+        q, k, v = run.step_inputs(st)
+        o_g = torch.full_like(q, float("nan"))
+        g = cb.cb_graph_create(run.shape, st.num_tokens, q, k, v, run.k_cache, run.v_cache, wl.scale, o_g)
+        try:
+            cb.cb_graph_step(g, st.num_reqs, st.num_tokens, st.max_blocks_per_req, st.cu_q_lens, st.ctx_lens,
+                             st.block_tables, run.stream)
+            torch.cuda.synchronize()
+        finally:
+            cb.cb_graph_destroy(g)
+    assert torch.equal(o_mixed, base)
+    assert torch.equal(o_g, base)
+    check(base, oracle_full(wl, step), "bf16", f"prefill_heads={heads} mixed/graph")

@@ -36,7 +36,7 @@ def describe(reqs, hq, hkv, d=128, dtype="bf16", **tune):
         return cb.cb_plan_describe(shape, batch(reqs))
     finally:
         defaults = {"split_blocks": 0, "target_waves": 0, "prefill_waves": 0, "decode_order": 1,
-                    "mixed_launch": 0, "prefill_split_tiles": 0, "decode_mfma": 1}
+                    "mixed_launch": 0, "prefill_split_tiles": 0, "decode_mfma": 1, "prefill_heads": 0}
         for k in tune:
             cb.cb_set_tuning(k, defaults[k])
 
@@ -51,9 +51,11 @@ def test_long_chunks_take_256_row_work_groups():
 
 def test_short_fresh_chunks_take_128_row_work_groups():
     """Many short fresh prompts (the trace's steps): enough 256-row tiles, but only about 4
-    key tiles each, so 128-row work-groups, two per CU."""
+    key tiles each, so 4-wave work-groups, two per CU; with 8 query heads per kv head each
+    takes 4 heads x 32 rows."""
     info = describe([(256, 0)] * 16 + [(1, 700)] * 8, 64, 8)
-    assert info["prefill_rows"] == 128
+    assert info["prefill_rows"] * info["prefill_heads"] == 128
+    assert info["prefill_heads"] == 4
 
 
 def test_late_chunk_takes_256_rows_split_over_key_ranges():
@@ -119,7 +121,7 @@ def test_mixed_launch_needs_both_kinds_of_rows():
     """With mixed_launch set, a bf16 step with prefill chunks and matrix-core decode rows
     takes one launch; a decode-only step does not."""
     both = describe([(300, 0), (1, 900), (1, 2000)], 16, 2, mixed_launch=1)
-    assert both["mixed"] == 1 and both["prefill_rows"] == 128
+    assert both["mixed"] == 1 and both["prefill_rows"] * both["prefill_heads"] == 128   # 4-wave groups
     decode_only = describe([(1, 900), (1, 2000)], 16, 2, mixed_launch=1)
     assert decode_only["mixed"] == 0
 
@@ -143,3 +145,14 @@ def test_rejects_a_batch_that_overflows_its_block_table():
     b.max_blocks_per_req = 2                     # 110 positions need 7 blocks
     with pytest.raises(cb.CbError):
         cb.cb_plan_describe(shape, b)
+
+
+@pytest.mark.parametrize("heads,hq,hkv,waves,rows,got_heads", [
+    (8, 64, 8, 8, 32, 8), (4, 64, 8, 8, 64, 4), (8, 8, 2, 8, 64, 4), (8, 64, 8, 4, 32, 4), (2, 32, 32, 8, 256, 1)])
+def test_prefill_heads_cut_rows(heads, hq, hkv, waves, rows, got_heads):
+    """prefill_heads: a work-group takes up to that many query heads of one kv head (capped by
+    the group size and the waves), and its rows shrink to 32 x waves / heads."""
+    d = describe([(300, 100)], hq, hkv, prefill_heads=heads, prefill_waves=waves)
+    assert (d["prefill_heads"], d["prefill_rows"]) == (got_heads, rows), d
+    tiles = -(-300 // rows)
+    assert d["prefill_items"] >= tiles * hq // got_heads
