@@ -18,10 +18,18 @@
 //                            B = P^T, which is exactly the S^T accumulator layout
 // with v_mfma_f32_32x32x16_bf16. Each lane owns one query column, so the row max, the
 // rescale factor and the row sum are per-lane values. Only the two lane halves (keys split
-// across lanes l and l^32) exchange the max. Within a 16-key MFMA step the key order is
-// permuted identically for A and B, so that P needs no shuffles. Tiles that lie past every
-// row of a wave are skipped, and the causal mask is only evaluated on tiles that cross the
-// diagonal.
+// across lanes l and l^32) exchange the max. The K rows are fed to the score MFMA in a
+// permuted order (see compute_s) that makes the S^T accumulator hold each lane's keys in
+// natural order, so P^T needs no shuffles and V^T is read as it is stored. Tiles that lie
+// past every row of a wave are skipped, and the causal mask is only evaluated on tiles that
+// cross the diagonal.
+//
+// Key and value tiles go from the cache straight into LDS (global_load_lds_dwordx4: no
+// staging registers and no LDS store instructions) through two K buffers and two V
+// buffers. Tile t's keys are first read one step before its values (the scores of tile t
+// are computed while tile t-1's probabilities are applied), so K(t+3) and V(t+2) are
+// requested right after the barrier that ends step t, and waited for at the end of step
+// t+1: one barrier per tile.
 #pragma once
 
 #include "cb_device.h"
@@ -30,13 +38,11 @@ namespace cb {
 
 template <int D>
 struct PrefillGeom {
-  static constexpr int KS = D + 8;                    // K tile row stride (elements)
-  static constexpr int VS = kPrefillKeys + 8;         // V^T tile row stride (elements, 16-B rows)
-  static constexpr int K_TILE = kPrefillKeys * KS;
-  static constexpr int V_TILE = D * VS;
-  static constexpr int LDS_ELEMS = 2 * (K_TILE + V_TILE);
-  static constexpr int DCH = D / 16;                  // MFMA k-steps over the head dim
-  static constexpr int DT = D / 32;                   // 32-wide output tiles over the head dim
+  static constexpr int PAGE_BYTES = kBlockSize * D * 2;   // one cache page: 16 positions x D bf16
+  static constexpr int TILE_BYTES = 4 * PAGE_BYTES;       // 64 keys
+  static constexpr int IPP = PAGE_BYTES / 1024;           // 1-KB direct loads per page (D / 32)
+  static constexpr int DCH = D / 16;                      // MFMA k-steps over the head dim
+  static constexpr int DT = D / 32;                       // 32-wide output tiles over the head dim
 };
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
@@ -48,15 +54,38 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16 bytes at byte offset `off` (per lane) of the buffer `rs` into LDS at lds_base + lane * 16
+// (lds_base uniform). The buffer form (not the flat global one): the compiler counts a flat
+// access to LDS as able to finish out of order with LDS reads, and would then make every
+// wait for an LDS operand a full wait.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base), 16, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt not waited for): every global load of this wave,
+// the direct-to-LDS ones included, has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // One prefill work-group's tile (work-group `slot` of the launch order). Every thread of the
-// work-group calls it; it holds the LDS staging buffers of the kernel that inlines it.
+// work-group calls it; it holds the LDS buffers of the kernel that inlines it.
 template <int D, int NW>
 __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   using Geo = PrefillGeom<D>;
-  constexpr int NT = 64 * NW;                           // threads
   constexpr int ROWS = 32 * NW;                         // row x head pairs of the work-group
-  constexpr int KS = Geo::KS, VS = Geo::VS, DCH = Geo::DCH, DT = Geo::DT;
-  __shared__ __align__(16) uint16_t lds[Geo::LDS_ELEMS];
+  constexpr int DCH = Geo::DCH, DT = Geo::DT, PAGE = Geo::PAGE_BYTES, IPP = Geo::IPP;
+  // LDS layout of one tile (4 pages of 16 positions):
+  //   K buffer: page p at p*PAGE, stored chunk-major: the 16-byte chunk c (elements
+  //     8c..8c+7) of position r at c*256 + r*16. A score MFMA operand (16 lanes on 16
+  //     positions, one chunk) then spans all 64 banks, and the chunks of an operand
+  //     differ by a constant offset.
+  //   V buffer: page p at p*PAGE, d-row d (the page's 16 positions of dimension d, 32 bytes)
+  //     at d*32, its two 8-position halves swapped in rows with bit 3 of d set (half h at
+  //     16*(h ^ bit3(d))), so a P.V operand (16 lanes on 16 d-rows, one half) spans all 64
+  //     banks.
+  // Each buffer is its own array, so that the compiler sees that a direct load into one
+  // buffer never aliases a read of another and adds no waits for it.
+  __shared__ __align__(1024) uint8_t kb0[Geo::TILE_BYTES], kb1[Geo::TILE_BYTES];
+  __shared__ __align__(1024) uint8_t vb0[Geo::TILE_BYTES], vb1[Geo::TILE_BYTES];
 
   if (a.desc) resolve_desc(a);
   if (slot >= a.n_items) return;                              // past a replayed step's items
@@ -70,8 +99,6 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   const int t0 = a.cu_q_lens[r];
   const int nq = a.cu_q_lens[r + 1] - t0;
   const int c = a.ctx_lens[r];
-  const int kv_len = c + nq;
-  const int tid = threadIdx.x;
   const int lane = lane_id(), wave = wave_id();
   const int col = lane & 31, grp = lane >> 5;
   const int h = it.head + (wave & ((1 << hl) - 1));          // this wave's query head
@@ -83,9 +110,8 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   const int kt0 = it.kt_begin;                                // absolute first key tile
   const int n_tiles = it.kt_end - kt0;                        // tiles of this item (local 0..)
   const int32_t* bt = a.block_tables + it.bt_row;
-  const int64_t page_elems = static_cast<int64_t>(kBlockSize) * D;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache);
 
   // the wave's query rows as the B operand of K Q^T: Q[qrow][16*dc + 8*grp .. +8]
   bf16x8 qf[DCH];
@@ -99,68 +125,70 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     }
   }
 
-  // global -> registers for key tile j. Every load instruction of a wave reads one page of
-  // the tile (positions 64j+16p .. +15), so its block id is a scalar and each thread's offset
-  // inside the page is fixed: K row tl/(D/8), chunk tl%(D/8); V^T bytes tl*16 (d-row tl/2,
-  // key octet tl%2). At D = 128 a page is one 16-byte chunk per thread (4 loads cover the 4
-  // pages); at D = 64 the two halves of the work-group take two pages per load. Only the
-  // tile that reaches wg_keys (the last key any row of this work-group sees) clamps pages
-  // and zeroes positions past it.
-  constexpr int TPP = 2 * D;                                       // threads per page (16 B each)
-  constexpr int PPL = NT / TPP;                                    // pages per load
-  constexpr int NL = 4 / PPL;                                      // loads per tile
-  static_assert(NL * PPL == 4, "a tile is 4 pages");
-  // Register staging: with 8 waves (one work-group per CU) there are registers for two
-  // sets, so tiles are requested two steps before they are stored to LDS; with 4 waves one.
-  constexpr int NSET = NW == 8 ? 2 : 1;
-  u32x4 kreg[NSET][NL], vreg[NSET][NL];
-  const int tl = tid % TPP;                                        // thread within its page
-  // Block id of key page pidx (clamped to the last page the work-group sees). The index is
-  // wave-uniform, so the id comes through the scalar cache straight into a scalar register;
-  // ids outside the pool read block 0.
+  // Direct loads: a tile is 4 * IPP 1-KB pieces of keys and as many of values; wave w takes
+  // pieces w*LPW .. w*LPW+LPW-1, which all lie in page pw of the tile. Each lane's source
+  // offset inside its cache page is fixed; only the page's block id changes from tile to
+  // tile (one id per wave and tile, a scalar).
+  constexpr int LPW = 4 * IPP / NW;                                // pieces per wave per tile
+  static_assert(LPW >= 1 && LPW * NW == 4 * IPP, "pieces must divide evenly over the waves");
+  const int pw = wave * LPW / IPP;                                 // page of this wave's pieces
+  uint32_t ksrc[LPW], vsrc[LPW], kdst[LPW], vdst[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int part = (wave * LPW + u) % IPP;                       // piece within the page
+    // keys: chunks 4*part .. 4*part+3 of positions 0..15 (lane: chunk 4*part + lane/16,
+    // position lane%16)
+    ksrc[u] = (lane % 16) * (2 * D) + (4 * part + lane / 16) * 16;
+    kdst[u] = pw * PAGE + part * 1024;
+    // values: d-rows 32*part .. +31 (lane: row 32*part + lane/2, stored half lane%2)
+    const int d = 32 * part + lane / 2;
+    vsrc[u] = d * 32 + ((lane & 1) ^ ((d >> 3) & 1)) * 16;
+    vdst[u] = pw * PAGE + part * 1024;
+  }
+  // Block id of key page pidx (clamped to the last page the work-group sees; ids outside the
+  // pool read block 0). The index is wave-uniform.
   const int last_page = __builtin_amdgcn_readfirstlane((wg_keys - 1) / kBlockSize);
-  auto page_block = [&](int pidx) -> int {
-    const int i = __builtin_amdgcn_readfirstlane(min(pidx, last_page));
-    const int blk = __builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(bt + i));
-    return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0;
+  auto page_of = [&](int t) { return min((kt0 + t) * 4 + pw, last_page); };   // this wave's page of tile t
+  auto valid_block = [&](int blk) { return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0; };
+  auto block_scalar = [&](int t) {
+    return valid_block(__builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(bt + page_of(t))));
   };
-  auto load_tile = [&](int j, int set) {
+  // a buffer resource over one cache page (its byte range bounds the lanes' offsets)
+  auto page_rsrc = [&](const uint8_t* cache, int blk) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache + (static_cast<int64_t>(blk) * hkv + g) * PAGE),
+                                             0, PAGE, kBufferFlags);
+  };
+  auto load_k = [&](uint8_t* dst, int blk) {
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(kc, blk);
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int page = u * PPL + tid / TPP;                // wave-uniform
-      const int64_t base = (static_cast<int64_t>(page_block(j * 4 + page)) * hkv + g) * page_elems;
-      kreg[set][u] = *reinterpret_cast<const u32x4*>(kc + base + (tl / (D / 8)) * D + (tl % (D / 8)) * 8);
-      vreg[set][u] = *reinterpret_cast<const u32x4*>(vc + base + tl * 8);
-    }
-    if ((j + 1) * kPrefillKeys > wg_keys) {        // the last tile: zero keys >= wg_keys
+    for (int u = 0; u < LPW; ++u) load_to_lds(rs, ksrc[u], dst + kdst[u]);
+  };
+  auto load_v = [&](uint8_t* dst, int blk) {
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(vc, blk);
 #pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const int page = u * PPL + tid / TPP;
-        const int kpos = j * kPrefillKeys + page * kBlockSize + tl / (D / 8);
-        if (kpos >= wg_keys) kreg[set][u] = u32x4{0u, 0u, 0u, 0u};
-        const int vpos = j * kPrefillKeys + page * kBlockSize + (tl % 2) * 8;
+    for (int u = 0; u < LPW; ++u) load_to_lds(rs, vsrc[u], dst + vdst[u]);
+  };
+  // The tile that reaches wg_keys (the last key any row of this work-group sees): value
+  // positions at or past it may hold anything (stale slots of the last page, or pages past
+  // it, clamped to it), and a zero probability times a non-finite value is not zero, so each
+  // lane zeroes them in the 16-byte pieces it loaded itself (after its own loads landed).
+  auto zero_tail = [&](uint8_t* vbuf, int t) {
+    const int lim = wg_keys - (kt0 + t) * kPrefillKeys;            // valid positions of the tile
+    if (lim >= kPrefillKeys) return;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int p0 = vpos + 2 * w;
-          vreg[set][u][w] &= (p0 < wg_keys ? 0x0000ffffu : 0u) | (p0 + 1 < wg_keys ? 0xffff0000u : 0u);
-        }
+    for (int u = 0; u < LPW; ++u) {
+      const int part = (wave * LPW + u) % IPP;
+      const int d = 32 * part + lane / 2;
+      const int hf = (lane & 1) ^ ((d >> 3) & 1);                  // half of the page held here
+      const int k0 = pw * kBlockSize + hf * 8;                     // its first position in the tile
+      if (k0 + 8 > lim) {
+        u32x4* q = reinterpret_cast<u32x4*>(vbuf + vdst[u] + lane * 16);
+        u32x4 v = *q;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          v[w] &= (k0 + 2 * w < lim ? 0x0000ffffu : 0u) | (k0 + 2 * w + 1 < lim ? 0xffff0000u : 0u);
+        *q = v;
       }
-    }
-  };
-  auto store_tile = [&](int buf, int set) {
-    uint16_t* kl = lds + buf * Geo::K_TILE;
-    uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int page = u * PPL + tid / TPP;
-      *reinterpret_cast<u32x4*>(kl + (page * kBlockSize + tl / (D / 8)) * KS + (tl % (D / 8)) * 8) = kreg[set][u];
-      // Inside each 16-key page, key k sits at position (k&3) + 4*(k>>3) + 8*((k>>2)&1):
-      // positions 0..7 then hold keys 0-3 and 8-11, positions 8..15 keys 4-7 and 12-15, the
-      // two key sets that lanes 0-31 and 32-63 take in one 32x32x16 step (the S^T accumulator
-      // layout). The thread's octet tl%2 = h (keys 8h..8h+7) goes to positions 4h.. and 8+4h..
-      uint16_t* vrow = vl + (tl / 2) * VS + page * kBlockSize + (tl % 2) * 4;
-      *reinterpret_cast<u32x2*>(vrow) = u32x2{vreg[set][u][0], vreg[set][u][1]};
-      *reinterpret_cast<u32x2*>(vrow + 8) = u32x2{vreg[set][u][2], vreg[set][u][3]};
     }
   };
 
@@ -172,9 +200,18 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   float m_run = -INFINITY, l_run = 0.f;
   const int qpos = c + qrow;
 
-  // S^T for the 64 keys of the tile in LDS buffer `buf`: two 32-key accumulators
-  auto compute_s = [&](int buf, f32x16 (&st)[2]) {
-    const uint16_t* kl = lds + buf * Geo::K_TILE;
+  // Operand addresses (bytes inside a buffer). Score MFMA: lane (col, grp) supplies row
+  // `col` of the 32-key block, fed from key position perm(col), where perm swaps bits 2 and
+  // 3 of the position inside each group of 16: the accumulator element (i, j) of lane grp
+  // (row 8i + 4grp + j) then holds key 16*(i/2) + 8*grp + 4*(i%2) + j, i.e. the 16-key step
+  // i/2 of the P.V product finds its 8 keys in natural order at 8*grp.. (its B operand), and
+  // the V^T operand is 8 consecutive positions of one d-row.
+  const int kperm = (col & 3) | ((col & 4) << 1) | ((col & 8) >> 1);
+  const int ka_off = (col >> 4) * PAGE + grp * 256 + kperm * 16;     // + kt*2*PAGE + dc*512
+  const int va_off = col * 32 + ((grp ^ (col >> 3)) & 1) * 16;       // + dt*1024 + ks*PAGE
+
+  // S^T for the 64 keys of the tile in K buffer kbuf: two 32-key accumulators
+  auto compute_s = [&](const uint8_t* kbuf, f32x16 (&st)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -183,7 +220,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     for (int dc = 0; dc < DCH; ++dc)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {   // two independent accumulation chains, interleaved
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kl + (kt * 32 + col) * KS + dc * 16 + grp * 8);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf + ka_off + kt * 2 * PAGE + dc * 512);
         st[kt] = mfma32(ka, qf[dc], st[kt]);
       }
   };
@@ -202,24 +239,25 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
 
-  // One key tile j whose scores are in s_cur and whose unmasked row max is mx: mask,
-  // softmax, O += V P. The scores of tile j+1 (other LDS buffer) are computed into s_next in
-  // the same straight-line block as the exp2 work of tile j, and their row max at its end,
-  // beside the P.V MFMAs, so the matrix core and the vector ALU overlap within the wave.
-  // Only tiles that cross the causal diagonal need a mask (every key of another tile is
-  // visible to every row of the wave), and only those recompute the max after it.
-  auto tile_step = [&](int u, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], float& mx) {
-    const int buf = u & 1;                       // local index: buffers and register sets
+  // One key tile u whose scores are in s_cur and whose unmasked row max is mx: mask,
+  // softmax, O += V P, with the tile's values in vbuf. The scores of tile u+1 (K buffer knext)
+  // are computed into s_next in the same straight-line block as the exp2 work of tile u, and
+  // their row max at its end, beside the P.V MFMAs, so the matrix core and the vector ALU
+  // overlap within the wave. Only tiles that cross the causal diagonal need a mask (every key
+  // of another tile is visible to every row of the wave), and only those recompute the max
+  // after it.
+  auto tile_step = [&](int u, const uint8_t* vbuf, const uint8_t* knext, f32x16 (&s_cur)[2],
+                       f32x16 (&s_next)[2], float& mx) {
     const int j = kt0 + u;                       // absolute tile: positions and masks
     if (!wave_active || j * kPrefillKeys >= wave_keys) return;
     const bool diag = __builtin_amdgcn_readfirstlane(j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0);
     if (diag) {                                  // causal mask, only on tiles crossing it
-      const int rel = qpos - j * kPrefillKeys - grp * 4;
+      const int rel = qpos - j * kPrefillKeys - grp * 8;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kt * 32 + (i >> 2) * 8 + (i & 3) > rel) s_cur[kt][i] = -INFINITY;
+          if (kt * 32 + (i >> 3) * 16 + ((i >> 2) & 1) * 4 + (i & 3) > rel) s_cur[kt][i] = -INFINITY;
       mx = tile_max(s_cur);
     }
     // Lazy rescaling: the reference max only moves when some lane's max grew by more than
@@ -236,7 +274,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
     }
-    compute_s(buf ^ 1, s_next);
+    compute_s(knext, s_next);
     const float m_ref = m_run;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};          // four independent sum chains
     bf16x8 pb[4];
@@ -255,14 +293,13 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
         pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
       }
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    // O^T += V^T P^T over four 16-key steps; one 16-byte read per A operand (the key order
-    // inside each 16-key page of the V^T tile matches the P layout, see store_tile)
-    const uint16_t* vl = lds + 2 * Geo::K_TILE + buf * Geo::V_TILE;
+    // O^T += V^T P^T over four 16-key steps (one per page of the tile); one 16-byte read per
+    // A operand: 8 consecutive positions of one d-row
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)               // DT independent accumulators back to back
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vl + (dt * 32 + col) * VS + grp * 8 + ks * 16);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbuf + va_off + dt * 1024 + ks * PAGE);
         oacc[dt] = mfma32(va, pb[ks], oacc[dt]);
       }
     mx = tile_max(s_next);
@@ -281,45 +318,57 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     }
   };
 
-  // prologue: tiles 0 and 1 in LDS, the scores of tile 0 computed, the next NSET tiles in
-  // flight (tile t is staged in register set t % NSET)
-  load_tile(kt0, 0);
-  store_tile(0, 0);
-  if (n_tiles > 1) load_tile(kt0 + 1, 1 % NSET);
+  // Block ids of the tiles requested at the next barrier (values of tile u+2, keys of tile
+  // u+3 after step u), loaded one step ahead into vector registers (all lanes read the same
+  // id): a scalar load in flight during a step would force full waits on the LDS operand
+  // reads, which share its counter.
+  int32_t id_v = 0, id_k = 0;
+  auto fetch_ids = [&](int tv, int tk) {
+    id_v = __builtin_nontemporal_load(bt + page_of(tv));
+    id_k = __builtin_nontemporal_load(bt + page_of(tk));
+  };
+
+  // prologue: keys of tiles 0 and 1 and values of tile 0 in LDS, the scores of tile 0, then
+  // the values of tile 1 and keys of tile 2 requested
+  load_k(kb0, block_scalar(0));
+  load_v(vb0, block_scalar(0));
+  if (n_tiles > 1) load_k(kb1, block_scalar(1));
+  wait_vmem();
+  if (n_tiles == 1) zero_tail(vb0, 0);
   __syncthreads();
   f32x16 sa[2], sb[2];
   float mx = 0.f;                                // unmasked row max of the next tile's scores
   if (wave_active) {
-    compute_s(0, sa);
+    compute_s(kb0, sa);
     mx = tile_max(sa);
   }
-  if (n_tiles > 1) {
-    store_tile(1, 1 % NSET);
-    if (n_tiles > 2) load_tile(kt0 + 2, 0);
-    if (NSET == 2 && n_tiles > 3) load_tile(kt0 + 3, 1 % NSET);
-  }
-  __syncthreads();
-  // Per tile j: step (reads buffer j&1, scores of j+1 from the other buffer), a barrier
-  // (buffer j&1 is free), tile j+2 from its register set into it, the loads of tile
-  // j+2+NSET into the same set, a barrier.
-  // (A variant with separate key and value buffer rings and one barrier per tile measured
-  // slower: the first barrier keeps the waves of the work-group in step.)
-  auto advance = [&](int j) {
+  __syncthreads();                               // K buffer 0 is read: it takes tile 2
+  if (n_tiles > 1) load_v(vb1, block_scalar(1));
+  if (n_tiles > 2) load_k(kb0, block_scalar(2));
+  fetch_ids(2, 3);
+  // After step u (values of tile u in V buffer u&1, keys of tile u+1 in K buffer (u+1)&1):
+  // wait for the requests of the previous barrier (values u+1, keys u+2, block ids), zero
+  // the last tile's value tail, barrier (both buffers of step u are free), then request
+  // values u+2 into V buffer u&1 and keys u+3 into K buffer (u+1)&1, and the block ids of
+  // the tiles after them.
+  auto advance = [&](int u, uint8_t* vfree, uint8_t* kfree, uint8_t* vnext) {
+    wait_vmem();
+    if (u + 1 == n_tiles - 1) zero_tail(vnext, u + 1);
     __syncthreads();
-    if (j + 2 < n_tiles) {
-      store_tile(j & 1, j % NSET);
-      if (j + 2 + NSET < n_tiles) load_tile(kt0 + j + 2 + NSET, j % NSET);
-    }
-    __syncthreads();
+    const int blk_v = valid_block(__builtin_amdgcn_readfirstlane(id_v));
+    const int blk_k = valid_block(__builtin_amdgcn_readfirstlane(id_k));
+    if (u + 2 < n_tiles) load_v(vfree, blk_v);
+    if (u + 3 < n_tiles) load_k(kfree, blk_k);
+    fetch_ids(u + 3, u + 4);
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile_step(j, sa, sb, mx);
-    advance(j);
-    if (j + 1 < n_tiles) {
-      tile_step(j + 1, sb, sa, mx);
-      advance(j + 1);
-    }
+  int u = 0;
+  for (; u + 1 < n_tiles; u += 2) {
+    tile_step(u, vb0, kb1, sa, sb, mx);
+    advance(u, vb0, kb1, vb1);
+    tile_step(u + 1, vb1, kb0, sb, sa, mx);
+    if (u + 2 < n_tiles) advance(u + 1, vb1, kb0, vb0);
   }
+  if (u < n_tiles) tile_step(u, vb0, kb1, sa, sb, mx);
 
   if (!wave_active) return;
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);

@@ -17,6 +17,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource word 3 for CDNA: 32-bit data format, no swizzle, raw (stride 0) access.
+constexpr int kBufferFlags = 0x00020000;
+
 // bf16 stored as 16-bit patterns; a 32-bit word holds two (low half = lower address).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

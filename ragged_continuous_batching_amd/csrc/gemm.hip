@@ -24,8 +24,6 @@ namespace {
 
 constexpr int kGM = 128;                          // rows (tokens) per work-group
 constexpr int kXcds = 8;                          // XCDs work-groups are dealt over (MI355X)
-// Buffer resource word 3 for CDNA: 32-bit data format, no swizzle, raw (stride 0) access.
-constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ f32x16 mfma_g(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
