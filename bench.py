@@ -166,6 +166,10 @@ def main(argv=None):
                          "continuous batching, naive padded batching (batch 32 and 8) and request-at-a-time, "
                          "all through the same kernels")
     ap.add_argument("--requests", type=int, default=256)
+    ap.add_argument("--compare-policies-trace", action="store_true",
+                    help="the config-5 trace itself (500 steps, the same Poisson arrivals) under continuous "
+                         "batching, naive padded batching (32, 8) and request-at-a-time: generated tokens/s "
+                         "and the pad and idle rows each policy processes")
     ap.add_argument("--layer", action="store_true",
                     help="config 2 with the token-wise projections around attention (Llama-2-7B shapes, "
                          "d_model 4096, synthetic bf16 weights): fused QKV projection + paged append, "
@@ -211,6 +215,8 @@ def main(argv=None):
         cb.cb_set_tuning(key, int(val))
     if args.compare_policies:
         return bench_policies(args)
+    if args.compare_policies_trace:
+        return bench_policies_trace(args)
     if args.layer:
         return bench_layer(args)
     if args.copy_calibration:
@@ -896,6 +902,133 @@ def bench_policies(args):
                    "generated_tokens": gen, "useful_rows": useful},
         "policies": out,
         "continuous_over": {n: round(base / v["generated_tokens_per_s"], 2) for n, v in out.items() if n != "continuous"},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def classify_rows(step, prompt, out, gen):
+    """(real rows, pad rows, idle rows, emitted tokens) of one built step; `gen` (request id ->
+    tokens generated so far) is advanced. Request r's known sequence is its prompt and the
+    tokens generated so far (positions < prompt + gen); a step's rows beyond it are pads of a
+    padded prefill (more than one row) or idle rows of a batch member that has finished. A step
+    emits a token for r when it processes the sequence's last known position and r still owes
+    tokens."""
+    real = pad = idle = emitted = 0
+    cu = step.cu_q_lens
+    for i in range(step.num_reqs):
+        rid = int(step.req_ids[i])
+        c, q = int(step.ctx_lens[i]), int(cu[i + 1] - cu[i])
+        P, O, g = prompt[rid], out[rid], gen.get(rid, 0)
+        n_real = max(0, min(c + q, P + g) - c)
+        real += n_real
+        if q > 1:
+            pad += q - n_real
+        else:
+            idle += q - n_real
+        if g < O and c <= P - 1 + g < c + q:
+            gen[rid] = g + 1
+            emitted += 1
+    return real, pad, idle, emitted
+
+
+def bench_policies_trace(args):
+    """The config-5 scheduler trace itself, 500 steps with the same Poisson arrivals, under
+    each policy the pages compare continuous batching with (zhangchitc "Naive batching";
+    hassanahmed's request-at-a-time serving): continuous batching (m = 4096), naive padded
+    batches of 32 and 8, and request-at-a-time. Same kernels, entry point and cache; only the
+    step builder's policy differs. A host-only dry run of each schedule classifies its rows
+    (real, pad, idle) and counts the tokens it emits; the timed run then replays the same
+    schedule through cb_step_forward. Throughput = tokens emitted in the 500 steps / wall
+    time."""
+    import torch
+
+    import workloads as W
+    from ragged_continuous_batching_amd import cb
+    from ragged_continuous_batching_amd.runner import DeviceRun
+
+    wl = W.config(5)
+    prompt = {r.req_id: r.prompt_len for k in range(wl.steps) for r in wl.arrivals[k]}
+    out = {r.req_id: r.out_len for k in range(wl.steps) for r in wl.arrivals[k]}
+    run = DeviceRun(wl, stale=None)
+    stream = torch.cuda.current_stream()
+    policies = [("continuous", 0), ("naive-batch-32", 32), ("naive-batch-8", 8), ("request-at-a-time", 1)]
+
+    def fresh(b):
+        s = cb.Scheduler(wl.token_budget, wl.block_size, wl.num_blocks, wl.max_num_seqs, wl.free_list)
+        if b:
+            s.set_static(b)
+        return s
+
+    stats, max_t, max_ws = {}, 1, 256
+    for name, b in policies:
+        s, gen = fresh(b), {}
+        tot = {"steps": 0, "empty_steps": 0, "rows": 0, "real_rows": 0, "pad_rows": 0, "idle_rows": 0,
+               "generated_tokens": 0}
+        for k in range(wl.steps):
+            for r in wl.arrivals[k]:
+                s.add(r.req_id, r.prompt_len, r.out_len)
+            st = s.build()
+            if st.num_reqs:
+                max_t = max(max_t, st.num_tokens)
+                max_ws = max(max_ws, cb.cb_step_workspace_size(run.shape, st.num_reqs, st.num_tokens,
+                                                               st.max_blocks_per_req, st.cu_q_lens, st.ctx_lens))
+                real, pad, idle, emitted = classify_rows(st, prompt, out, gen)
+                tot["rows"] += st.num_tokens
+                tot["real_rows"] += real
+                tot["pad_rows"] += pad
+                tot["idle_rows"] += idle
+                tot["generated_tokens"] += emitted
+            else:
+                tot["empty_steps"] += 1
+            tot["steps"] += 1
+            s.commit()
+        tot["requests_finished"] = sum(1 for rid, g in gen.items() if g >= out[rid])
+        tot["requests_arrived"] = len(prompt)
+        stats[name] = tot
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    q = torch.randn(max_t, wl.num_q_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    k_new = torch.randn(max_t, wl.num_kv_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    v_new = torch.randn(max_t, wl.num_kv_heads, wl.head_dim, device="cuda", generator=g).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    ws = torch.empty(max_ws, dtype=torch.uint8, device="cuda")
+
+    def drive(s, steps):
+        for k in range(steps):
+            for r in wl.arrivals[k]:
+                s.add(r.req_id, r.prompt_len, r.out_len)
+            st = s.build_raw()
+            if st.num_reqs:
+                launch_step(cb, run, st, q, k_new, v_new, o, ws, stream)
+            s.commit()
+
+    drive(fresh(0), 100)                          # warm-up (clocks, code objects)
+    torch.cuda.synchronize()
+    results = {}
+    for name, b in policies:
+        s = fresh(b)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        drive(s, wl.steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = stats[name]
+        results[name] = dict(st, seconds=round(wall, 4),
+                             generated_tokens_per_s=round(st["generated_tokens"] / wall, 1),
+                             real_row_fraction=round(st["real_rows"] / max(1, st["rows"]), 4),
+                             ms_per_step=round(wall * 1e3 / wl.steps, 4))
+    base = results["continuous"]["generated_tokens_per_s"]
+    result = {
+        "metric": "generated tokens/s over the 500-step trace, per scheduling policy",
+        "value": base, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "scheduler-trace replay (500 steps, Poisson(8) arrivals per step, lognormal "
+                               "prompts, geometric outputs), the same arrivals for every policy",
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "token_budget": wl.token_budget},
+        "policies": results,
+        "continuous_over": {n: round(base / v["generated_tokens_per_s"], 2) for n, v in results.items()
+                            if n != "continuous" and v["generated_tokens_per_s"] > 0},
     }
     print(json.dumps(result), flush=True)
     return 0

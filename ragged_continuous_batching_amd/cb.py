@@ -13,7 +13,9 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcb.so")
+# CB_LIBRARY names another build of the same library to load instead (the host-sanitized
+# test copy); by default the in-tree libcb.so.
+LIB_PATH = os.environ.get("CB_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcb.so")
 
 CB_OK = 0
 CB_ERR_INVALID_ARG = -1
