@@ -132,18 +132,20 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   constexpr int LPW = 4 * IPP / NW;                                // pieces per wave per tile
   static_assert(LPW >= 1 && LPW * NW == 4 * IPP, "pieces must divide evenly over the waves");
   const int pw = wave * LPW / IPP;                                 // page of this wave's pieces
-  uint32_t ksrc[LPW], vsrc[LPW], kdst[LPW], vdst[LPW];
+  // piece u of this wave: its place in the page, and its LDS offset in a buffer (wave-uniform,
+  // recomputed where used rather than kept in scalar registers through the loop)
+  auto piece = [&](int u) { return (wave * LPW + u) % IPP; };
+  auto piece_lds = [&](int u) { return static_cast<uint32_t>(pw * PAGE + piece(u) * 1024); };
+  uint32_t ksrc[LPW], vsrc[LPW];
 #pragma unroll
   for (int u = 0; u < LPW; ++u) {
-    const int part = (wave * LPW + u) % IPP;                       // piece within the page
+    const int part = piece(u);
     // keys: chunks 4*part .. 4*part+3 of positions 0..15 (lane: chunk 4*part + lane/16,
     // position lane%16)
     ksrc[u] = (lane % 16) * (2 * D) + (4 * part + lane / 16) * 16;
-    kdst[u] = pw * PAGE + part * 1024;
     // values: d-rows 32*part .. +31 (lane: row 32*part + lane/2, stored half lane%2)
     const int d = 32 * part + lane / 2;
     vsrc[u] = d * 32 + ((lane & 1) ^ ((d >> 3) & 1)) * 16;
-    vdst[u] = pw * PAGE + part * 1024;
   }
   // Block id of key page pidx (clamped to the last page the work-group sees; ids outside the
   // pool read block 0). The index is wave-uniform.
@@ -161,12 +163,12 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   auto load_k = [&](uint8_t* dst, int blk) {
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(kc, blk);
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) load_to_lds(rs, ksrc[u], dst + kdst[u]);
+    for (int u = 0; u < LPW; ++u) load_to_lds(rs, ksrc[u], dst + piece_lds(u));
   };
   auto load_v = [&](uint8_t* dst, int blk) {
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(vc, blk);
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) load_to_lds(rs, vsrc[u], dst + vdst[u]);
+    for (int u = 0; u < LPW; ++u) load_to_lds(rs, vsrc[u], dst + piece_lds(u));
   };
   // The tile that reaches wg_keys (the last key any row of this work-group sees): value
   // positions at or past it may hold anything (stale slots of the last page, or pages past
@@ -177,12 +179,12 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     if (lim >= kPrefillKeys) return;
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
-      const int part = (wave * LPW + u) % IPP;
+      const int part = piece(u);
       const int d = 32 * part + lane / 2;
       const int hf = (lane & 1) ^ ((d >> 3) & 1);                  // half of the page held here
       const int k0 = pw * kBlockSize + hf * 8;                     // its first position in the tile
       if (k0 + 8 > lim) {
-        u32x4* q = reinterpret_cast<u32x4*>(vbuf + vdst[u] + lane * 16);
+        u32x4* q = reinterpret_cast<u32x4*>(vbuf + piece_lds(u) + lane * 16);
         u32x4 v = *q;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
