@@ -278,7 +278,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     }
     compute_s(knext, s_next);
     const float m_ref = m_run;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};          // four independent sum chains
+    float ps[4];                                 // four independent sum chains
     bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -289,7 +289,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][half * 8 + 2 * e], a.scale_log2, -m_ref));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kt][half * 8 + 2 * e + 1], a.scale_log2, -m_ref));
-          ps[kt * 2 + half] += p0 + p1;
+          ps[kt * 2 + half] = e == 0 ? p0 + p1 : ps[kt * 2 + half] + (p0 + p1);   // no add of 0 first
           w[e] = pack_bf16x2(p0, p1);
         }
         pb[kt * 2 + half] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
