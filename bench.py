@@ -410,6 +410,13 @@ def bench_fixed(args, cfg, cpu_budget_s=25.0):
         "algorithmic": alg,
         "attention_tokens_per_s": round(T / (sum(kernels[k]["avg_us"] for k in kernels if k != "append") * 1e-6), 1),
     }
+    if dominant == "decode" and "prefill" in kernels and alg["prefill"]["flops"] > 0:
+        # the prefill rows of a decode-dominated step, timed alone: their own MFMA fraction
+        pre_s = kernels["prefill"]["avg_us"] * 1e-6
+        pre_tf = alg["prefill"]["flops"] / pre_s / 1e12
+        result["prefill_roofline"] = {"bound": "mfma", "achieved": round(pre_tf, 1), "peak": BF16_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(pre_tf / BF16_PEAK_TFLOPS, 4),
+                                      "kernel": "prefill_kernel", "timed_steps": kernels["prefill"]["timed_steps"]}
     if args.graph:
         result["eager"] = {"value": result["value"], "ms_per_step": result["ms_per_step"],
                            "device_ms_per_step": result["device_ms_per_step"]}
