@@ -13,8 +13,8 @@ Prints one JSON line. ``roofline`` describes the dominant kernel: average durati
 hipEvents recorded by the library on the kernel's own stream during the timed steps, and
 algorithmic bytes (each visible K/V position read once, Q read once, O written once) or
 algorithmic flops (unmasked pairs only). ``traffic`` comes from the committed rocprofv3
-counter summary of that kernel (profiles/*_pmc.json) and is null when the kernel source has
-changed since the counters were taken. ``cpu_baseline`` times the fp64 oracle on the host.
+counter summary of that kernel (profiles/*_pmc.json) and is null when the kernel's code
+(comments aside) has changed since the counters were taken. ``cpu_baseline`` times the fp64 oracle on the host.
 """
 from __future__ import annotations
 
@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,11 +54,19 @@ def algorithmic(wl, step):
     return out
 
 
+def code_text(src):
+    """C/C++ source without comments and blank lines: what the compiler sees of it."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def source_sha(*names):
+    """Hash of the code (comments ignored) of the named csrc files."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "ragged_continuous_batching_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "ragged_continuous_batching_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -2,8 +2,9 @@
 //
 // Hugging Face blog "Continuous batching from first principles": scores cost O(n^2 d)
 // (section "Attention"); a chunk attends to the cached keys of its own request plus its own
-// keys, with the causal mask cut "in the middle" (section "Chunked prefill"); requests
-// never see each other (section "Continuous batching"). zhangchitc "continuous-batching":
+// keys, its rows sitting after the cached positions so the causal mask is aligned to the
+// bottom right (section "Chunked prefill"); requests never see each other (section
+// "Continuous batching"). zhangchitc "continuous-batching":
 // masked pairs are not computed at all, and the cache is read one block at a time into a
 // running online-softmax state.
 //
@@ -24,7 +25,7 @@
 // past every row of a wave are skipped, and the causal mask is only evaluated on tiles that
 // cross the diagonal.
 //
-// Key and value tiles go from the cache straight into LDS (global_load_lds_dwordx4: no
+// Key and value tiles go from the cache straight into LDS (buffer_load_dwordx4 ... lds: no
 // staging registers and no LDS store instructions) through two K buffers and two V
 // buffers. Tile t's keys are first read one step before its values (the scores of tile t
 // are computed while tile t-1's probabilities are applied), so K(t+3) and V(t+2) are
@@ -128,7 +129,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   // Direct loads: a tile is 4 * IPP 1-KB pieces of keys and as many of values; wave w takes
   // pieces w*LPW .. w*LPW+LPW-1, which all lie in page pw of the tile. Each lane's source
   // offset inside its cache page is fixed; only the page's block id changes from tile to
-  // tile (one id per wave and tile, a scalar).
+  // tile (one id per wave and tile, the same in every lane).
   constexpr int LPW = 4 * IPP / NW;                                // pieces per wave per tile
   static_assert(LPW >= 1 && LPW * NW == 4 * IPP, "pieces must divide evenly over the waves");
   const int pw = wave * LPW / IPP;                                 // page of this wave's pieces
