@@ -222,6 +222,31 @@ void make_plan(const cb_shape* s, const cb_batch* b, Plan& p, int force_waves, b
   // interleaved into the launch order. Unused slots hold an empty item (req = -1).
   if (!groups.empty()) {
     const int nx = std::max(1, g_tuning.xcds);
+    // A group costlier than one XCD's share of the step (the long chunk of a request with
+    // few kv heads: one or two groups hold nearly all the work) is cut, in item order, into
+    // pieces of about that share, so it does not leave the other XCDs idle.
+    int64_t total_cost = 0;
+    for (const PrefillGroup& grp : groups) total_cost += grp.cost;
+    const int64_t share = (total_cost + nx - 1) / nx;
+    std::vector<PrefillGroup> pieces;
+    for (PrefillGroup& grp : groups) {
+      if (grp.cost <= share || grp.items.size() < 2) {
+        pieces.push_back(std::move(grp));
+        continue;
+      }
+      PrefillGroup cur;
+      for (const PrefillItem& it : grp.items) {
+        const int64_t c = it.kt_end - it.kt_begin;
+        if (cur.cost > 0 && cur.cost + c > share) {
+          pieces.push_back(std::move(cur));
+          cur = PrefillGroup();
+        }
+        cur.items.push_back(it);
+        cur.cost += c;
+      }
+      if (!cur.items.empty()) pieces.push_back(std::move(cur));
+    }
+    groups.swap(pieces);
     std::stable_sort(groups.begin(), groups.end(),
                      [](const PrefillGroup& x, const PrefillGroup& y) { return x.cost > y.cost; });
     std::vector<std::vector<PrefillItem>> queue(nx);

@@ -153,6 +153,22 @@ def test_small_steps_full_oracle(name, hq, hkv, d, dtype):
     check(o, oracle_full(wl, step), dtype, f"{name} Hq={hq} Hkv={hkv} D={d} {dtype}")
 
 
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(8, 1, 128, "bf16"), (2, 1, 64, "f32")])
+def test_very_long_contexts(hq, hkv, d, dtype):
+    """The largest contexts of any test: a decode row after 131,071 cached tokens (8192 cache
+    blocks: thousands of short decode splits merged by one combine row), a 100-row chunk
+    after 65,536 cached tokens (1026 key tiles per item, split over key ranges), and a fresh
+    prompt. Every row against the oracle."""
+    reqs = [W.Request(0, 131071, 1 << 20, cached=131071, generated=1),
+            W.Request(1, 65636, 1 << 20, cached=65536, generated=0),
+            W.Request(2, 70, 1 << 20)]
+    wl = W.custom(reqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype, seed=11)
+    run, step, batch, o = run_one_step(wl)
+    assert list(np.diff(step.cu_q_lens)) == [1, 100, 70] and list(step.ctx_lens) == [131071, 65536, 0]
+    rows, ref = oracle_rows(wl, step, range(step.num_tokens))
+    check(o[torch.from_numpy(rows).cuda()], ref, dtype, f"very long contexts Hq={hq} Hkv={hkv} D={d} {dtype}")
+
+
 def test_small_steps_normal_values_unit_scale():
     """Sharper softmax (scale 1, N(0,1) values) on the same ragged mix."""
     wl = small_workload("mixed", 8, 2, 128, "bf16")

@@ -156,3 +156,15 @@ def test_prefill_heads_cut_rows(heads, hq, hkv, waves, rows, got_heads):
     assert (d["prefill_heads"], d["prefill_rows"]) == (got_heads, rows), d
     tiles = -(-300 // rows)
     assert d["prefill_items"] >= tiles * hq // got_heads
+
+
+def test_a_dominant_group_is_cut_across_xcds():
+    """A 100-row chunk after 65,536 cached tokens with one kv head: its split items all belong
+    to one (request, kv head) group, which would put them on one XCD (1952 launch slots, 7 of
+    8 XCDs idle). The group is cut into pieces of about one XCD's share, so the launch order
+    holds the 248 items in 8 near-even queues."""
+    info = describe([(1, 131071), (100, 65536), (70, 0)], 8, 1)
+    assert info["prefill_split_items"] == 244
+    assert info["prefill_items"] <= 8 * (-(-248 // 8) + 4), info
+    # a step whose groups are all below the share keeps one group per XCD queue as before
+    assert describe([(2048, 2048), (2048, 6144), (2048, 14336), (2048, 0)], 32, 32)["prefill_items"] == 1024
