@@ -228,18 +228,23 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
       }
   };
 
-  // Row max of a 64-key score tile (four independent chains, then lanes l and l^32)
+  // Row max of a 64-key score tile (four independent chains, then lanes l and l^32). The
+  // NaN-propagating maximum (v_maximum3_f32) needs no quieting of its MFMA-result inputs,
+  // which fmaxf does (one extra instruction per chain); the scores it sees are finite or
+  // -inf, except past the end of a request, which only diagonal tiles hold and which are
+  // masked and their max taken again before use.
   auto tile_max = [&](const f32x16 (&st)[2]) -> float {
     float mq[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) mq[q] = fmaxf(st[q >> 1][(q & 1) * 8], st[q >> 1][(q & 1) * 8 + 1]);
+    for (int q = 0; q < 4; ++q) mq[q] = __builtin_elementwise_maximum(st[q >> 1][(q & 1) * 8], st[q >> 1][(q & 1) * 8 + 1]);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 2; i < 8; ++i) mq[q] = fmaxf(mq[q], st[q >> 1][(q & 1) * 8 + i]);
-    const float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+      for (int i = 2; i < 8; ++i) mq[q] = __builtin_elementwise_maximum(mq[q], st[q >> 1][(q & 1) * 8 + i]);
+    const float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
+                                                   __builtin_elementwise_maximum(mq[2], mq[3]));
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
 
   // One key tile u whose scores are in s_cur and whose unmasked row max is mx: mask,
