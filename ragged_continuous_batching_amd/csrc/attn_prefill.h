@@ -258,7 +258,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
                        f32x16 (&s_next)[2], float& mx) {
     const int j = kt0 + u;                       // absolute tile: positions and masks
     if (!wave_active || j * kPrefillKeys >= wave_keys) return;
-    const bool diag = __builtin_amdgcn_readfirstlane(j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0);
+    const bool diag = j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0;   // uniform (scalar) values
     if (diag) {                                  // causal mask, only on tiles crossing it
       const int rel = qpos - j * kPrefillKeys - grp * 8;
 #pragma unroll
@@ -273,7 +273,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     // hold as well as values below 1; O and l share the reference, so O / l is unchanged.
     // The scale is positive, so max(scale*s) = scale*max(s) and it folds into the fma.
     const float m_cand = fmaxf(m_run, mx * a.scale_log2);
-    if (__builtin_amdgcn_readfirstlane(__ballot(m_cand > m_run + 8.f) != 0)) {
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + 8.f) != 0) {   // wave-uniform: a scalar branch
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
       m_run = m_cand;
       l_run *= alpha;
