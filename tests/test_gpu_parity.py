@@ -377,6 +377,23 @@ def test_config4_chunked_prefill():
     check(o[torch.from_numpy(rows).cuda()], ref, "bf16", "config 4 (chunk edges)")
 
 
+def test_largest_step():
+    """A step four times config 4's width: 32,768 packed rows (a decode row and fifteen
+    2048-row chunks after contexts 0..28,672, one 2047-row chunk), Hq = 8, Hkv = 1. Sampled
+    rows (first and last rows of each chunk, work-group edges) against the oracle; the decode
+    row too."""
+    reqs = [W.Request(0, 3000, 1 << 20, cached=3000, generated=1)]
+    for i in range(15):
+        c = 2048 * i
+        reqs.append(W.Request(1 + i, c + 2048, 1 << 20, cached=c, generated=0))
+    reqs.append(W.Request(16, 2047, 1 << 20))
+    wl = W.custom(reqs, num_q_heads=8, num_kv_heads=1, head_dim=128, dtype="bf16", seed=13)
+    run, step, batch, o = run_one_step(wl)
+    assert step.num_tokens == 1 + 15 * 2048 + 2047 == 32768
+    rows, ref = oracle_rows(wl, step, chunk_edge_rows(step, tile=40, boundary=512))
+    check(o[torch.from_numpy(rows).cuda()], ref, "bf16", f"largest step ({len(rows)} sampled rows)")
+
+
 def test_config5_trace_replay():
     """500 steps of the scheduler trace with append + attention every step. The first and the
     last row of every request in the contiguous window of steps 150..199 (about 30k rows;
