@@ -89,6 +89,8 @@ def _load():
                                                      ctypes.c_int32, P, P]),
         "cb_step_forward": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            P, P, P, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "cb_step_slots": (ctypes.c_int, [ctypes.POINTER(cb_shape), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         P, P, P, P]),
         "cb_last_error": (ctypes.c_char_p, []),
         "cb_version": (ctypes.c_char_p, []),
         "cb_set_tuning": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
@@ -130,7 +132,7 @@ lib = _load()
 EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_plan_describe", "cb_ragged_attention",
             "cb_ragged_attention_noalloc",
             "cb_step_workspace_size",
-            "cb_step_forward", "cb_last_error",
+            "cb_step_forward", "cb_step_slots", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_get_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
             "cb_profile_reset", "cb_profile_select",
             "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
@@ -215,6 +217,19 @@ def cb_step_workspace_size(shape: cb_shape, num_reqs: int, num_tokens: int, max_
     (cu, _a), (ctx, _b) = _host_i32(h_cu_q_lens), _host_i32(h_ctx_lens)
     return int(lib.cb_step_workspace_size(ctypes.byref(shape), int(num_reqs), int(num_tokens), int(max_blocks_per_req),
                                           cu, ctx))
+
+
+CB_SLOT_SOLE_WRITER = 1 << 30
+
+
+def cb_step_slots(shape: cb_shape, num_reqs: int, num_tokens: int, max_blocks_per_req: int, h_cu_q_lens, h_ctx_lens,
+                  h_block_tables) -> np.ndarray:
+    """The cache slot of every packed row as the step entry points stage it (host only)."""
+    (cu, _a), (ctx, _b), (bt, _c) = _host_i32(h_cu_q_lens), _host_i32(h_ctx_lens), _host_i32(h_block_tables)
+    out = np.zeros(max(int(num_tokens), 0), np.int32)
+    _check(lib.cb_step_slots(ctypes.byref(shape), int(num_reqs), int(num_tokens), int(max_blocks_per_req), cu, ctx,
+                             bt, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
 
 
 def cb_step_forward(shape: cb_shape, num_reqs: int, num_tokens: int, max_blocks_per_req: int, h_cu_q_lens,

@@ -496,6 +496,9 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   // slots and the compact block table go together: with them, no kernel indexes the table
   // by max_blocks_per_req (the append takes slots, the rest take each item's bt_row)
   const bool slots = slots_fit(shape);
+  // Marked rows need the staging kernel: their (row, slot) list stays in the pinned buffer,
+  // after the bytes the append copies into the workspace, and the page work-groups read it there.
+  const bool marks = slots && sole_marks_fit(shape) && g_tuning.stage_kernel;
   std::vector<int32_t> bt_rows;
   const int64_t nbt = slots ? compact_rows(num_reqs, h_cu_q_lens, h_ctx_lens, bt_rows)
                             : static_cast<int64_t>(num_reqs) * max_blocks_per_req;
@@ -514,16 +517,20 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
                 l.plan_base + p.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(CB_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
-  // one upload: metadata, then the plan
+  // one upload: metadata, then the plan (then, not copied, the marked rows)
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t staged = l.plan_base + p.plan_bytes;
+  const size_t off_marked = (staged + 15) & ~static_cast<size_t>(15);
+  int32_t n_marked = 0;
   auto fill = [&](char* host) {
     std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
     std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
     if (slots) {
       fill_compact(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, bt_rows,
                    reinterpret_cast<int32_t*>(host + l.off_bt));
-      fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
-                 reinterpret_cast<int32_t*>(host + l.off_slots));
+      n_marked = fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
+                            reinterpret_cast<int32_t*>(host + l.off_slots), marks,
+                            marks ? reinterpret_cast<int32_t*>(host + off_marked) : nullptr);
     } else {
       std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
     }
@@ -531,17 +538,21 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   };
   AppendArgs aa{k_new, v_new, k_cache, v_cache, b.cu_q_lens, b.ctx_lens, b.block_tables, num_reqs, num_tokens,
                 max_blocks_per_req, shape->num_kv_heads, shape->num_blocks, nullptr,
-                slots ? reinterpret_cast<const int32_t*>(ws + l.off_slots) : nullptr, nullptr, nullptr, 0};
+                slots ? reinterpret_cast<const int32_t*>(ws + l.off_slots) : nullptr, nullptr, nullptr, 0,
+                marks ? kSlotSoleWriter : 0};
   const int eb = elem_bytes(shape);
   hipError_t e = hipSuccess;
   if (g_tuning.stage_kernel && slots) {
     // The append launch also moves the staged bytes into the workspace, and takes its slots
     // straight from the pinned buffer: one kernel fewer per step.
-    st = upload_with(l.plan_base + p.plan_bytes, s, fill, [&](const void* src_dev, const void*, size_t n) {
+    const size_t up = marks ? off_marked + static_cast<size_t>(num_tokens) * 8 : staged;
+    st = upload_with(up, s, fill, [&](const void* src_dev, const void*, size_t) {
       aa.slots = reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + l.off_slots);
       aa.stage_src = src_dev;
       aa.stage_dst = ws;
-      aa.stage_n16 = static_cast<int64_t>(n / 16);
+      aa.stage_n16 = static_cast<int64_t>((staged + 15) / 16);
+      aa.marked = n_marked ? reinterpret_cast<const int32_t*>(static_cast<const char*>(src_dev) + off_marked) : nullptr;
+      aa.n_marked = n_marked;
       ProfScope prof(CB_KERNEL_APPEND, s);
       return e = launch_kv_append(aa, eb, shape->head_dim, s);
     });
@@ -553,6 +564,28 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   }
   if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_step_forward: append launch failed: %s", hipGetErrorString(e));
   return launch_attention(shape, &b, p, ws + l.plan_base, q, k_cache, v_cache, scale, o, s, true);
+}
+
+static_assert(kSlotSoleWriter == CB_SLOT_SOLE_WRITER, "the staged sole-writer bit is the one cb.h documents");
+
+extern "C" int cb_step_slots(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens, int32_t max_blocks_per_req,
+                             const int32_t* h_cu_q_lens, const int32_t* h_ctx_lens, const int32_t* h_block_tables,
+                             int32_t* out_slots) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (num_reqs < 0 || max_blocks_per_req < 0) return fail(CB_ERR_INVALID_ARG, "cb_step_slots: negative count");
+  cb_batch b = step_batch(num_reqs, num_tokens, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, nullptr,
+                          step_layout(num_reqs, 0, num_tokens));
+  if ((st = check_batch(shape, &b))) return st;
+  if (num_tokens == 0) return CB_OK;
+  if (!out_slots) return fail(CB_ERR_INVALID_ARG, "cb_step_slots: out_slots is null");
+  if (!slots_fit(shape)) return fail(CB_ERR_UNSUPPORTED, "cb_step_slots: the pool is too large for host slots");
+  if ((st = check_block_ids(shape, num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
+                            "cb_step_slots")))
+    return st;
+  fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, out_slots,
+             sole_marks_fit(shape));
+  return CB_OK;
 }
 
 extern "C" int cb_linear(int32_t M, int32_t N, int32_t K, const void* a, const void* w, void* c, void* stream) {

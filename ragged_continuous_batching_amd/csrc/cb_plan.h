@@ -91,7 +91,20 @@ struct AppendArgs {
   const void* stage_src;
   void* stage_dst;
   int64_t stage_n16;
+  // kSlotSoleWriter when the host marks slots (see below), else 0: the bit is then part of
+  // the slot value.
+  int32_t sole_bit;
+  // The marked rows as (packed row, slot) pairs, n_marked of them, read by the page
+  // work-groups that follow the rows' (kPageRows marked rows each); null with n_marked = 0.
+  const int32_t* marked;
+  int32_t n_marked;
 };
+
+// Set in a host slot when its row is the only row of the step that writes into its block (a
+// decode row, unless requests share a block): the append then rewrites that block's whole V^T
+// page instead of one element per d-row. Used while num_blocks * block_size fits below the bit.
+constexpr int32_t kSlotSoleWriter = 1 << 30;
+constexpr int kPageRows = 2;             // marked rows per page work-group
 
 struct RowArgs {
   const void* q;

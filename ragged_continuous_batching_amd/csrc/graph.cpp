@@ -353,7 +353,7 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
     fill_compact(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, bt_rows,
                  reinterpret_cast<int32_t*>(host + l.off_bt));
     fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
-               reinterpret_cast<int32_t*>(host + l.off_slots));
+               reinterpret_cast<int32_t*>(host + l.off_slots), false);   // replays write V^T element-wise
   } else {
     std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
   }

@@ -18,7 +18,7 @@ namespace cb {
 hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int head_dim, hipStream_t s);
 // Grid of kv_append_kernel for num_tokens rows (256-thread work-groups); launch_kv_append and
 // the captured step both take it from here.
-dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim);
+dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim, int32_t n_marked = 0);
 hipError_t launch_rows(const RowArgs& a, int elem_bytes, int head_dim, int group, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int waves, hipStream_t s);
@@ -114,11 +114,16 @@ struct StepLayout {
 
 // bt_entries: block-table entries staged (the compact table's length, or R * max_blocks).
 StepLayout step_layout(int32_t R, int64_t bt_entries, int32_t T);
-// Cache slot of every packed row from the host metadata.
-void fill_slots(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt, int32_t* out);
+// Cache slot of every packed row from the host metadata; with `mark`, rows that are the only
+// row of the step writing into their block also carry kSlotSoleWriter, and `marked` (room for
+// 2 * T values, or null) receives their (row, slot) pairs. Returns the number of marked rows.
+int32_t fill_slots(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt, int32_t* out,
+                   bool mark, int32_t* marked = nullptr);
 // Slots fit an int32 for every pool this library accepts in practice; larger pools keep the
 // device-side lookup.
 inline bool slots_fit(const cb_shape* s) { return s->num_blocks <= INT32_MAX / kBlockSize; }
+// The sole-writer bit stays clear of every slot value (pools up to 2^26 blocks).
+inline bool sole_marks_fit(const cb_shape* s) { return s->num_blocks <= kSlotSoleWriter / kBlockSize; }
 // Offsets of each request's block ids in the compact table; returns the entry count.
 int64_t compact_rows(int32_t R, const int32_t* cu, const int32_t* ctx, std::vector<int32_t>& rows);
 void fill_compact(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt,

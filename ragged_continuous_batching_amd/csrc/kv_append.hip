@@ -16,8 +16,17 @@
 //   2. K chunks go straight to their slots (key rows stay contiguous); V rows are staged in
 //      LDS;
 //   3. V^T leaves LDS per d-row: a group of 16/ES rows that occupies consecutive, aligned
-//      slots of one block (rows of a prefill chunk) is written as one 16-byte store; other
-//      rows (decode rows, the edges of a chunk) element by element, as the layout implies.
+//      slots of one block (rows of a prefill chunk) is written as one 16-byte store;
+//   4. other rows (decode rows, the edges of a chunk) are written element by element, except
+//      rows the host marks as the only row of the step writing into their block (decode
+//      rows, as a rule): extra work-groups at the end of the grid, two marked rows each,
+//      rewrite those blocks' whole V^T pages. A page is read, the row's element put into
+//      each d-row, and every chunk stored back, the other slots with their own bits. One
+//      element per 32-byte d-row leaves partly written cache lines, which memory merges
+//      later at the cost of a read and a write each: skipping those writes altogether (a
+//      timing copy) took 12-13 us off a step of 64 decode rows x 32 kv heads or 256 x 8,
+//      most of it in the kernels after the append.
+#include <algorithm>
 #include <type_traits>
 
 #include "cb_device.h"
@@ -33,6 +42,57 @@ constexpr int append_heads() {
   return 256 / (16 * (D * ES / 16)) > 1 ? 256 / (16 * (D * ES / 16)) : 1;
 }
 
+// Whole V^T pages of marked rows m0 .. m0 + kPageRows - 1, kv heads g0 .. g0 + nheads - 1.
+// Chunk c of a page holds d-row c / CPR, slots (c % CPR) * VEC ..; the chunk that holds the
+// row's slot takes its new element (straight from v_new), every other one keeps its bits.
+// All chunks are loaded before any is stored.
+template <int ES, int D, int HEADS>
+__device__ __forceinline__ void append_pages(const AppendArgs& a, int m0, int g0, int nheads, int tid) {
+  constexpr int VEC = 16 / ES;
+  constexpr int PCH = D * kBlockSize * ES / 16;        // 16-byte chunks per V^T page
+  constexpr int CPR = kBlockSize / VEC;                // chunks per d-row
+  constexpr int NCH = kPageRows * HEADS * PCH / 256;   // chunks per thread
+  static_assert(NCH * 256 == kPageRows * HEADS * PCH, "page chunks must split evenly over 256 threads");
+  using E = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
+  u32x4 buf[NCH];
+  int64_t at[NCH];                                     // chunk index in the V cache, -1: none
+  uint32_t val[NCH], keep[NCH];                        // new element in place; bits kept
+  int dw[NCH];                                         // dword that takes it, -1: none
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int w = tid + u * 256;
+    const int c = w % PCH, hh = (w / PCH) % HEADS, m = m0 + w / (PCH * HEADS);
+    at[u] = -1;
+    dw[u] = -1;
+    val[u] = 0u;
+    keep[u] = 0xffffffffu;
+    if (m >= a.n_marked || hh >= nheads) continue;
+    const int t = a.marked[2 * m], sl = a.marked[2 * m + 1];
+    const int blk = sl / kBlockSize, off = sl % kBlockSize;
+    if (sl < 0 || static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks) ||
+        static_cast<unsigned>(t) >= static_cast<unsigned>(a.num_tokens))
+      continue;
+    at[u] = (static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh) * PCH + c;
+    buf[u] = reinterpret_cast<const u32x4*>(a.v_cache)[at[u]];
+    if (c % CPR == off / VEC) {
+      const int e = off % VEC, sh = (e * ES % 4) * 8;
+      dw[u] = e * ES / 4;
+      keep[u] = ES == 4 ? 0u : ~(0xffffu << sh);
+      val[u] = static_cast<uint32_t>(
+                   static_cast<const E*>(a.v_new)[(static_cast<int64_t>(t) * a.num_kv_heads + g0 + hh) * D + c / CPR])
+               << sh;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    if (at[u] < 0) continue;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k == dw[u]) buf[u][k] = (buf[u][k] & keep[u]) | val[u];
+    reinterpret_cast<u32x4*>(a.v_cache)[at[u]] = buf[u];
+  }
+}
+
 template <int ES, int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   constexpr int VEC = 16 / ES;              // elements per 16-byte chunk
@@ -43,10 +103,14 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   __shared__ __align__(16) E vt[HEADS * ROWS * LS];
   __shared__ int32_t info_blk[ROWS], info_off[ROWS];
   __shared__ int32_t info_run[ROWS / VEC];
+  __shared__ uint32_t info_sole;               // bit r: row r rewrites its whole V^T page
 
   if (a.desc) resolve_desc(a);
+  const int n_groups = (a.num_tokens + ROWS - 1) / ROWS;
+  const bool pages = static_cast<int>(blockIdx.x) >= n_groups;   // a whole-page work-group
   const int t0 = blockIdx.x * ROWS;
-  if (t0 >= a.num_tokens) return;              // past the live rows of a replayed step
+  if (pages && (static_cast<int>(blockIdx.x) - n_groups) * kPageRows >= a.n_marked)
+    return;                                    // past the live rows of a replayed step
   const int g0 = blockIdx.y * HEADS;
   const int tid = threadIdx.x;
   const int nrows = min(ROWS, a.num_tokens - t0);
@@ -79,12 +143,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     for (int64_t i = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 256 + tid; i < n16; i += stride)
       dst[i] = src[i];
   }
+  if (pages) {
+    append_pages<ES, D, HEADS>(a, (blockIdx.x - n_groups) * kPageRows, g0, nheads, tid);
+    return;
+  }
   if (tid < ROWS) {
     int blk = -1, off = 0;
+    bool sole = false;
     if (tid < nrows) {
       const int t = t0 + tid;
       if (a.slots) {                            // the host's slot: one load instead of a chain
-        const int sl = a.slots[t];
+        int sl = a.slots[t];
+        if (sl >= 0 && (sl & a.sole_bit) != 0) {
+          sole = true;
+          sl &= ~a.sole_bit;
+        }
         blk = sl >= 0 ? sl / kBlockSize : -1;
         off = sl >= 0 ? sl % kBlockSize : 0;
       } else {
@@ -97,6 +170,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     }
     info_blk[tid] = blk;
     info_off[tid] = off;
+    const uint64_t sole_rows = __ballot(sole && blk >= 0);   // the 16 lanes of wave 0
+    if (tid == 0) info_sole = static_cast<uint32_t>(sole_rows);
   }
   // V rows into LDS
 #pragma unroll
@@ -128,8 +203,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   __syncthreads();
 
   // V^T: a group of VEC rows that fill VEC consecutive, aligned slots of one block (the rows
-  // of a prefill chunk, as a rule) leaves as one 16-byte store per d-row; other groups (decode
-  // rows, chunk edges) store element by element.
+  // of a prefill chunk, as a rule) leaves as one 16-byte store per d-row; in other groups the
+  // unmarked rows store element by element and the marked ones are left to the page
+  // work-groups.
   constexpr int GROUPS = ROWS / VEC;
   for (int e = tid; e < HEADS * D * GROUPS; e += 256) {
     const int grp = e % GROUPS, d = (e / GROUPS) % D, hh = e / (GROUPS * D);
@@ -148,7 +224,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     } else {
       for (int i = 0; i < VEC && r0 + i < nrows; ++i) {
         const int blk = info_blk[r0 + i];
-        if (blk < 0) continue;
+        if (blk < 0 || ((info_sole >> (r0 + i)) & 1u)) continue;
         const int64_t page = static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh;
         static_cast<E*>(a.v_cache)[(page * D + d) * kBlockSize + info_off[r0 + i]] = src[i * LS];
       }
@@ -156,20 +232,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   }
 }
 
-dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim) {
+dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim, int32_t n_marked) {
   const int h = elem_bytes == 2 ? (head_dim == 128 ? append_heads<2, 128>() : append_heads<2, 64>())
                                 : (head_dim == 128 ? append_heads<4, 128>() : append_heads<4, 64>());
   // at least one work-group in each dimension (a captured step may replay with no rows; the
-  // kernel exits for rows and heads past the end)
-  const int64_t x = (num_tokens + 15) / 16, y = (num_kv_heads + h - 1) / h;
+  // kernel exits for rows and heads past the end); the page work-groups follow the rows'
+  const int64_t x = (num_tokens + 15) / 16 + (std::max(n_marked, 0) + kPageRows - 1) / kPageRows,
+                y = (num_kv_heads + h - 1) / h;
   return dim3(static_cast<unsigned>(x > 0 ? x : 1), static_cast<unsigned>(y > 0 ? y : 1));
 }
 
 template <int ES, int D>
 static hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL((kv_append_kernel<ES, D>), append_grid(a.num_tokens, a.num_kv_heads, ES, D), dim3(256), 0, s,
-                     a);
+  hipLaunchKernelGGL((kv_append_kernel<ES, D>), append_grid(a.num_tokens, a.num_kv_heads, ES, D, a.n_marked),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

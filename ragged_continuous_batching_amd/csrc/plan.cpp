@@ -4,6 +4,7 @@
 // code only.
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "host.h"
 
@@ -378,11 +379,62 @@ StepLayout step_layout(int32_t R, int64_t bt_entries, int32_t T) {
 // Cache slot (block * block_size + offset) of every packed row, from the host metadata
 // (the slot rule of cb_kv_append: row i of request r sits at position ctx_lens[r] + i).
 // Block ids were checked against the pool before this is called.
-void fill_slots(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt, int32_t* out) {
-  for (int32_t r = 0; r < R; ++r) {
-    const int32_t* row = bt + static_cast<size_t>(r) * maxb;
-    for (int32_t t = cu[r], p = ctx[r]; t < cu[r + 1]; ++t, ++p) out[t] = row[p / kBlockSize] * kBlockSize + p % kBlockSize;
+//
+// With `mark`, a row that is the only row of the step writing into its block also carries
+// kSlotSoleWriter. Rows are counted per block (not per request) in an open-addressing table
+// of the blocks the step writes, so a block that holds two rows of a chunk, or that two
+// requests share, is never marked.
+int32_t fill_slots(int32_t R, int32_t maxb, const int32_t* cu, const int32_t* ctx, const int32_t* bt, int32_t* out,
+                   bool mark, int32_t* marked) {
+  if (!mark) {
+    for (int32_t r = 0; r < R; ++r) {
+      const int32_t* row = bt + static_cast<size_t>(r) * maxb;
+      for (int32_t t = cu[r], p = ctx[r]; t < cu[r + 1]; ++t, ++p)
+        out[t] = row[p / kBlockSize] * kBlockSize + p % kBlockSize;
+    }
+    return 0;
   }
+  int32_t n_marked = 0;
+  thread_local std::vector<int32_t> keys;      // block id, -1: empty
+  thread_local std::vector<uint8_t> counts;    // rows written into it, saturating at 2
+  int bits = 6;
+  while ((size_t{1} << bits) < 2 * static_cast<size_t>(std::max(cu[R], 1))) ++bits;
+  const size_t mask = (size_t{1} << bits) - 1;
+  keys.assign(mask + 1, -1);
+  counts.assign(mask + 1, 0);
+  auto entry = [&](int32_t b) {                // Fibonacci hashing, linear probing
+    size_t h = (static_cast<uint32_t>(b) * 0x9E3779B1u) >> (32 - bits);
+    while (keys[h] != b && keys[h] != -1) h = (h + 1) & mask;
+    keys[h] = b;
+    return h;
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int32_t r = 0; r < R; ++r) {
+      const int32_t q = cu[r + 1] - cu[r];
+      if (q <= 0) continue;
+      const int32_t* row = bt + static_cast<size_t>(r) * maxb;
+      const int32_t p0 = ctx[r], p1 = ctx[r] + q - 1;
+      for (int32_t j = p0 / kBlockSize; j <= p1 / kBlockSize; ++j) {
+        const int32_t lo = std::max(p0, j * kBlockSize), hi = std::min(p1, j * kBlockSize + kBlockSize - 1);
+        const size_t h = entry(row[j]);
+        if (pass == 0) {
+          counts[h] = static_cast<uint8_t>(std::min(2, counts[h] + hi - lo + 1));
+        } else {
+          const int32_t flag = counts[h] == 1 ? kSlotSoleWriter : 0;
+          for (int32_t p = lo; p <= hi; ++p) {
+            const int32_t t = cu[r] + p - p0, slot = row[j] * kBlockSize + p % kBlockSize;
+            out[t] = slot | flag;
+            if (flag && marked) {
+              marked[2 * n_marked] = t;
+              marked[2 * n_marked + 1] = slot;
+            }
+            n_marked += flag != 0;
+          }
+        }
+      }
+    }
+  }
+  return n_marked;
 }
 
 

@@ -161,3 +161,57 @@ def check_cache_live(run, step):
     rids = step.req_ids[req]
     assert torch.equal(bits(run.k_cache[blk, :, off, :]), bits(run.gather(W.KIND_K, rids, pos)))
     assert torch.equal(bits(run.v_cache[blk, :, :, off]), bits(run.gather(W.KIND_V, rids, pos)))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_whole_page_rewrites_keep_every_other_slot(dtype, d):
+    """Rows alone in their block rewrite its whole transposed V page (cb_step_slots marks
+    them); the other positions of that page must come back with the bits they held (finite
+    values, and NaN where nothing was written). A hand-built step: decode rows alone in their
+    blocks, two decode rows whose requests share one block (not marked: each writes its
+    element), a chunk whose last row opens a new block, a chunk that crosses a block edge.
+    The whole cache is compared bit for bit with the expected one."""
+    hq, hkv, nb, bs = 4, 2, 48, 16
+    shape = cb.make_shape(hq, hkv, d, nb, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(11)
+    # (q_len, ctx, table)
+    reqs = [(1, 20, [3, 4]), (1, 5, [7]), (1, 2, [9]), (1, 6, [9]), (17, 16, [10, 11, 12]), (3, 30, [15, 13, 14]),
+            (1, 47, [20, 21, 22])]
+    cu = np.concatenate([[0], np.cumsum([r[0] for r in reqs])]).astype(np.int32)
+    ctx = np.array([r[1] for r in reqs], np.int32)
+    maxb = max(len(r[2]) for r in reqs)
+    bt = np.full((len(reqs), maxb), -1, np.int32)
+    for i, r in enumerate(reqs):
+        bt[i, :len(r[2])] = r[2]
+    T = int(cu[-1])
+    slots = cb.cb_step_slots(shape, len(reqs), T, maxb, cu, ctx, bt)
+    marked = (slots & cb.CB_SLOT_SOLE_WRITER) != 0
+    want = [True, True, False, False] + [False] * 16 + [True] + [False, False, True] + [True]
+    assert marked.tolist() == want
+    slots = slots & ~cb.CB_SLOT_SOLE_WRITER
+    # caches: referenced blocks hold finite values in their first half, NaN in the rest;
+    # unreferenced blocks are NaN
+    k_cache = torch.full((nb, hkv, bs, d), float("nan"), dtype=tdt)
+    v_cache = torch.full((nb, hkv, d, bs), float("nan"), dtype=tdt)
+    for b in sorted({b for r in reqs for b in r[2]}):
+        k_cache[b, :, :8, :] = torch.randn(hkv, 8, d, generator=g).to(tdt)
+        v_cache[b, :, :, :8] = torch.randn(hkv, d, 8, generator=g).to(tdt)
+    k_new = torch.randn(T, hkv, d, generator=g).to(tdt)
+    v_new = torch.randn(T, hkv, d, generator=g).to(tdt)
+    q = torch.randn(T, hq, d, generator=g).to(tdt)
+    k_exp, v_exp = k_cache.clone(), v_cache.clone()
+    for t in range(T):
+        b, o = int(slots[t]) // bs, int(slots[t]) % bs
+        k_exp[b, :, o, :] = k_new[t]
+        v_exp[b, :, :, o] = v_new[t]
+    kc, vc = k_cache.cuda(), v_cache.cuda()
+    qd, kd, vd = q.cuda(), k_new.cuda(), v_new.cuda()
+    out = torch.empty_like(qd)
+    need = cb.cb_step_workspace_size(shape, len(reqs), T, maxb, cu, ctx)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    cb.cb_step_forward(shape, len(reqs), T, maxb, cu, ctx, bt, qd, kd, vd, kc, vc, d ** -0.5, out, ws, need,
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(kc.cpu()), bits(k_exp))
+    assert torch.equal(bits(vc.cpu()), bits(v_exp))

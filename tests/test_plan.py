@@ -168,3 +168,126 @@ def test_a_dominant_group_is_cut_across_xcds():
     assert info["prefill_items"] <= 8 * (-(-248 // 8) + 4), info
     # a step whose groups are all below the share keeps one group per XCD queue as before
     assert describe([(2048, 2048), (2048, 6144), (2048, 14336), (2048, 0)], 32, 32)["prefill_items"] == 1024
+
+
+# ---- staged slots and sole-writer marks (cb_step_slots) -------------------------------------
+
+SOLE = cb.CB_SLOT_SOLE_WRITER
+
+
+def staged_slots(reqs, tables, num_blocks=4096):
+    """cb_step_slots for [(q_len, ctx_len), ...] with explicit per-request block lists."""
+    q = np.array([r[0] for r in reqs], np.int32)
+    c = np.array([r[1] for r in reqs], np.int32)
+    cu = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    maxb = max(1, max(len(t) for t in tables))
+    bt = np.full((len(reqs), maxb), -1, np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    shape = cb.make_shape(8, 8, 128, num_blocks, "bf16")
+    return cb.cb_step_slots(shape, len(reqs), int(cu[-1]), maxb, cu, c, bt), cu, c, bt
+
+
+def rule_slots(cu, ctx, bt, bs=16):
+    """The slot rule written out (cb_kv_append's): row i of request r at p = ctx[r] + i."""
+    out = []
+    for r in range(len(ctx)):
+        for i in range(cu[r + 1] - cu[r]):
+            p = ctx[r] + i
+            out.append(bt[r, p // bs] * bs + p % bs)
+    return np.array(out, np.int64)
+
+
+def brute_marks(slots, bs=16):
+    """A row is marked iff no other row of the step writes into its block."""
+    blocks = slots // bs
+    return np.array([(blocks == b).sum() == 1 for b in blocks], bool)
+
+
+def test_decode_rows_are_marked_and_chunk_rows_are_not():
+    # two decode rows, a chunk of 20 rows from position 0 (16 + 4 rows in two blocks), and a
+    # chunk of 17 rows from position 16 whose last row is alone in its block
+    reqs = [(1, 40), (1, 15), (20, 0), (17, 16)]
+    tables = [[5, 9, 11], [7], [20, 21], [30, 31, 32]]
+    out, cu, ctx, bt = staged_slots(reqs, tables)
+    assert np.array_equal(out & ~SOLE, rule_slots(cu, ctx, bt))
+    marked = (out & SOLE) != 0
+    assert np.array_equal(marked, brute_marks(rule_slots(cu, ctx, bt)))
+    assert marked[:2].all()                   # the decode rows
+    assert not marked[2:22].any()             # 16 + 4 rows in two blocks
+    assert not marked[22:38].any() and marked[38]   # positions 16..31 in block 31, 32 alone in block 32
+
+
+def test_rows_of_requests_sharing_a_block_are_not_marked():
+    """Two decode rows whose requests (wrongly) share their last block: neither may rewrite the
+    page, or one would overwrite the other's new position; a request with no rows shares
+    blocks without counting."""
+    reqs = [(1, 3), (1, 4), (0, 7), (1, 0)]
+    tables = [[8], [8], [40], [40]]
+    out, cu, ctx, bt = staged_slots(reqs, tables)
+    assert np.array_equal(out & ~SOLE, rule_slots(cu, ctx, bt))
+    assert ((out & SOLE) != 0).tolist() == [False, False, True]
+
+
+def test_marks_match_brute_force_on_a_random_permuted_pool():
+    """Many requests on a randomly permuted pool (so the marks' hash table sees collisions):
+    decode rows, chunks at every alignment, and a few requests sharing blocks."""
+    rng = np.random.default_rng(5)
+    reqs, tables = [], []
+    pool = rng.permutation(1 << 16).astype(np.int32)
+    nxt = 0
+    for _ in range(600):
+        q = int(rng.choice([1, 1, 1, 2, 7, 16, 33]))
+        c = int(rng.integers(0, 200))
+        nb = -(-(c + q) // 16)
+        t = pool[nxt:nxt + nb].tolist()
+        nxt += nb
+        if rng.random() < 0.02 and tables:    # share the previous request's blocks
+            t = (tables[-1] + t)[:nb] if len(tables[-1]) >= nb else t
+        reqs.append((q, c))
+        tables.append(t)
+    out, cu, ctx, bt = staged_slots(reqs, tables, num_blocks=1 << 16)
+    ref = rule_slots(cu, ctx, bt)
+    assert np.array_equal(out & ~SOLE, ref)
+    assert np.array_equal((out & SOLE) != 0, brute_marks(ref))
+    assert ((out & SOLE) != 0).sum() > 200
+
+
+def test_marks_stop_where_the_bit_would_be_a_slot_bit():
+    reqs, tables = [(1, 3)], [[5]]
+    out, *_ = staged_slots(reqs, tables, num_blocks=1 << 26)
+    assert out[0] == (5 * 16 + 3) | SOLE
+    out, *_ = staged_slots(reqs, tables, num_blocks=(1 << 26) + 1)
+    assert out[0] == 5 * 16 + 3
+    with pytest.raises(cb.CbError):            # beyond int32 slots: the device looks them up
+        staged_slots(reqs, tables, num_blocks=(1 << 27) + 1)
+
+
+def test_step_slots_checks_block_ids():
+    with pytest.raises(cb.CbError):
+        staged_slots([(1, 20)], [[3]])         # position 20 needs a second block id
+    with pytest.raises(cb.CbError):
+        staged_slots([(1, 3)], [[5000]], num_blocks=4096)
+
+
+def test_step_slots_agree_with_the_reference_scheduler():
+    """Along a reference-scheduler trace (arrivals, chunked prefill, decode, EOS), the staged
+    slots without their marks are the scheduler's slot mapping."""
+    from oracle.scheduler import RefScheduler
+    rng = np.random.default_rng(3)
+    s = RefScheduler(token_budget=256, block_size=16, num_blocks=2048)
+    rid = 0
+    for step_i in range(40):
+        for _ in range(int(rng.poisson(2))):
+            s.add(rid, int(rng.integers(1, 300)), int(rng.integers(1, 40)))
+            rid += 1
+        st = s.build()
+        if st.num_tokens == 0:
+            s.commit()
+            continue
+        shape = cb.make_shape(8, 8, 128, 2048, "bf16")
+        out = cb.cb_step_slots(shape, st.num_reqs, st.num_tokens, st.block_tables.shape[1], st.cu_q_lens,
+                               st.ctx_lens, st.block_tables)
+        assert np.array_equal(out & ~SOLE, st.slot_mapping), f"step {step_i}"
+        assert np.array_equal((out & SOLE) != 0, brute_marks(st.slot_mapping.astype(np.int64)))
+        s.commit()
