@@ -179,9 +179,10 @@ int cb_ragged_attention_noalloc(const cb_shape* shape, const cb_batch* batch, co
  *   q, k_new, v_new, k_cache, v_cache, scale, o: as in cb_kv_append / cb_ragged_attention.
  *   workspace: device, 256-byte aligned, at least cb_step_workspace_size() bytes; it holds
  *       the step's metadata, plan and partials and must not be shared by calls in flight.
- * A block that receives exactly one row of the step (see cb_step_slots) has its whole V
- * page rewritten, its other positions with the bits they already hold: nothing else may
- * write that block while the step runs (as for every block of a request in the step).
+ * In a step of decode rows only, a block that receives exactly one row (see cb_step_slots)
+ * has its whole V page rewritten, its other positions with the bits they already hold:
+ * nothing else may write that block while the step runs (as for every block of a request
+ * in the step).
  * ------------------------------------------------------------------------------------- */
 size_t cb_step_workspace_size(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
                               int32_t max_blocks_per_req, const int32_t* h_cu_q_lens,
@@ -198,12 +199,13 @@ int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
  * i of request r, at position p = h_ctx_lens[r] + i, goes to slot
  * block_tables[r][p / block_size] * block_size + p % block_size.
  *   out_slots  host int32 [num_tokens], written in full.
- * When num_blocks * block_size <= 2^30, a row that is the only row of the step writing into
- * its block (a decode row, unless two requests share the block) also carries bit 30
+ In a step of decode rows only (every request has at most one row) and when
+ * num_blocks * block_size <= 2^30, a row that is the only row of the step writing into its
+ * block (every row, unless two requests share a block) also carries bit 30
  * (CB_SLOT_SOLE_WRITER). For such rows cb_step_forward (with the default "stage_kernel")
  * rewrites the block's whole transposed V page, the other positions with the bits they hold,
- * so that the append writes whole cache lines; cb_graph_step and the copy-engine upload
- * stage the same slots without the bit and write one element per d-row.
+ * so that the append writes whole cache lines. Steps with prefill rows, cb_graph_step and
+ * the copy-engine upload stage slots without the bit and write one element per d-row.
  * Returns CB_OK; the argument errors of cb_step_forward's host checks (CB_ERR_INVALID_ARG,
  * out-of-range block ids included); CB_ERR_UNSUPPORTED for pools beyond 2^31 / block_size
  * blocks, whose steps look slots up on the device instead. */

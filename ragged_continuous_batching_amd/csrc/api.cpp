@@ -498,7 +498,7 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
   const bool slots = slots_fit(shape);
   // Marked rows need the staging kernel: their (row, slot) list stays in the pinned buffer,
   // after the bytes the append copies into the workspace, and the page work-groups read it there.
-  const bool marks = slots && sole_marks_fit(shape) && g_tuning.stage_kernel;
+  const bool marks = slots && g_tuning.stage_kernel && sole_marks_apply(shape, num_reqs, h_cu_q_lens);
   std::vector<int32_t> bt_rows;
   const int64_t nbt = slots ? compact_rows(num_reqs, h_cu_q_lens, h_ctx_lens, bt_rows)
                             : static_cast<int64_t>(num_reqs) * max_blocks_per_req;
@@ -584,7 +584,7 @@ extern "C" int cb_step_slots(const cb_shape* shape, int32_t num_reqs, int32_t nu
                             "cb_step_slots")))
     return st;
   fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, out_slots,
-             sole_marks_fit(shape));
+             sole_marks_apply(shape, num_reqs, h_cu_q_lens));
   return CB_OK;
 }
 

@@ -19,13 +19,14 @@
 //      slots of one block (rows of a prefill chunk) is written as one 16-byte store;
 //   4. other rows (decode rows, the edges of a chunk) are written element by element, except
 //      rows the host marks as the only row of the step writing into their block (decode
-//      rows, as a rule): extra work-groups at the end of the grid, two marked rows each,
-//      rewrite those blocks' whole V^T pages. A page is read, the row's element put into
+//      rows of a decode-only step): extra work-groups at the start of the grid, two marked
+//      rows each, rewrite those blocks' whole V^T pages. A page is read, the row's element put into
 //      each d-row, and every chunk stored back, the other slots with their own bits. One
 //      element per 32-byte d-row leaves partly written cache lines, which memory merges
 //      later at the cost of a read and a write each: skipping those writes altogether (a
 //      timing copy) took 12-13 us off a step of 64 decode rows x 32 kv heads or 256 x 8,
-//      most of it in the kernels after the append.
+//      most of it in the kernels after the append. A prefill kernel between the append and
+//      the decode rows hides that merge, so the host marks rows only in decode-only steps.
 #include <algorithm>
 #include <type_traits>
 
@@ -106,14 +107,14 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   __shared__ uint32_t info_sole;               // bit r: row r rewrites its whole V^T page
 
   if (a.desc) resolve_desc(a);
-  const int n_groups = (a.num_tokens + ROWS - 1) / ROWS;
-  const bool pages = static_cast<int>(blockIdx.x) >= n_groups;   // a whole-page work-group
-  const int t0 = blockIdx.x * ROWS;
-  if (pages && (static_cast<int>(blockIdx.x) - n_groups) * kPageRows >= a.n_marked)
-    return;                                    // past the live rows of a replayed step
+  // The page work-groups come first, so that their longer chains (pinned list, page, stores)
+  // start early; they load no rows.
+  const int n_pagex = (max(a.n_marked, 0) + kPageRows - 1) / kPageRows;
+  const bool pages = static_cast<int>(blockIdx.x) < n_pagex;     // a whole-page work-group
+  const int t0 = (static_cast<int>(blockIdx.x) - n_pagex) * ROWS;
   const int g0 = blockIdx.y * HEADS;
   const int tid = threadIdx.x;
-  const int nrows = min(ROWS, a.num_tokens - t0);
+  const int nrows = pages ? 0 : min(ROWS, a.num_tokens - t0);   // page work-groups load no rows
   const int nheads = min(HEADS, a.num_kv_heads - g0);
   // The new K and V chunks of the work-group are requested first; the slot lookup (a binary
   // search over cu_q_lens, then ctx_lens and the block table: a chain of dependent loads)
@@ -144,9 +145,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
       dst[i] = src[i];
   }
   if (pages) {
-    append_pages<ES, D, HEADS>(a, (blockIdx.x - n_groups) * kPageRows, g0, nheads, tid);
+    append_pages<ES, D, HEADS>(a, blockIdx.x * kPageRows, g0, nheads, tid);
     return;
   }
+  if (t0 >= a.num_tokens) return;              // past the live rows
   if (tid < ROWS) {
     int blk = -1, off = 0;
     bool sole = false;

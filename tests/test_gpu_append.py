@@ -163,21 +163,25 @@ def check_cache_live(run, step):
     assert torch.equal(bits(run.v_cache[blk, :, :, off]), bits(run.gather(W.KIND_V, rids, pos)))
 
 
+@pytest.mark.parametrize("with_chunk", [False, True])
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
-def test_whole_page_rewrites_keep_every_other_slot(dtype, d):
-    """Rows alone in their block rewrite its whole transposed V page (cb_step_slots marks
-    them); the other positions of that page must come back with the bits they held (finite
-    values, and NaN where nothing was written). A hand-built step: decode rows alone in their
-    blocks, two decode rows whose requests share one block (not marked: each writes its
-    element), a chunk whose last row opens a new block, a chunk that crosses a block edge.
-    The whole cache is compared bit for bit with the expected one."""
+def test_whole_page_rewrites_keep_every_other_slot(dtype, d, with_chunk):
+    """In a decode-only step, rows alone in their block rewrite its whole transposed V page
+    (cb_step_slots marks them); the other positions of that page must come back with the
+    bits they held (finite values, and NaN where nothing was written). A hand-built step:
+    decode rows alone in their blocks at the first, middle and last slot, and two decode rows
+    whose requests share one block (not marked: each writes its element). With a prefill
+    chunk added, no row is marked and every row writes element by element. The whole cache is
+    compared bit for bit with the expected one."""
     hq, hkv, nb, bs = 4, 2, 48, 16
     shape = cb.make_shape(hq, hkv, d, nb, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     g = torch.Generator().manual_seed(11)
     # (q_len, ctx, table)
-    reqs = [(1, 20, [3, 4]), (1, 5, [7]), (1, 2, [9]), (1, 6, [9]), (17, 16, [10, 11, 12]), (3, 30, [15, 13, 14]),
+    reqs = [(1, 20, [3, 4]), (1, 5, [7]), (1, 2, [9]), (1, 6, [9]), (1, 16, [10, 11]), (1, 31, [12, 13]),
             (1, 47, [20, 21, 22])]
+    if with_chunk:
+        reqs.append((17, 16, [30, 31, 32]))
     cu = np.concatenate([[0], np.cumsum([r[0] for r in reqs])]).astype(np.int32)
     ctx = np.array([r[1] for r in reqs], np.int32)
     maxb = max(len(r[2]) for r in reqs)
@@ -187,7 +191,7 @@ def test_whole_page_rewrites_keep_every_other_slot(dtype, d):
     T = int(cu[-1])
     slots = cb.cb_step_slots(shape, len(reqs), T, maxb, cu, ctx, bt)
     marked = (slots & cb.CB_SLOT_SOLE_WRITER) != 0
-    want = [True, True, False, False] + [False] * 16 + [True] + [False, False, True] + [True]
+    want = [False] * T if with_chunk else [True, True, False, False, True, True, True]
     assert marked.tolist() == want
     slots = slots & ~cb.CB_SLOT_SOLE_WRITER
     # caches: referenced blocks hold finite values in their first half, NaN in the rest;
