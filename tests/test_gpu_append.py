@@ -164,16 +164,18 @@ def check_cache_live(run, step):
 
 
 @pytest.mark.parametrize("with_chunk", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (6, 3)])
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
-def test_whole_page_rewrites_keep_every_other_slot(dtype, d, with_chunk):
+def test_whole_page_rewrites_keep_every_other_slot(dtype, d, hq, hkv, with_chunk):
     """In a decode-only step, rows alone in their block rewrite its whole transposed V page
     (cb_step_slots marks them); the other positions of that page must come back with the
     bits they held (finite values, and NaN where nothing was written). A hand-built step:
     decode rows alone in their blocks at the first, middle and last slot, and two decode rows
     whose requests share one block (not marked: each writes its element). With a prefill
     chunk added, no row is marked and every row writes element by element. The whole cache is
-    compared bit for bit with the expected one."""
-    hq, hkv, nb, bs = 4, 2, 48, 16
+    compared bit for bit with the expected one. Odd kv head counts leave the last page
+    work-group of two heads (D = 64 in bf16) with one."""
+    nb, bs = 48, 16
     shape = cb.make_shape(hq, hkv, d, nb, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     g = torch.Generator().manual_seed(11)
