@@ -202,9 +202,9 @@ int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens,
  In a step of decode rows only (every request has at most one row) and when
  * num_blocks * block_size <= 2^30, a row that is the only row of the step writing into its
  * block (every row, unless two requests share a block) also carries bit 30
- * (CB_SLOT_SOLE_WRITER). For such rows cb_step_forward (with the default "stage_kernel")
- * rewrites the block's whole transposed V page, the other positions with the bits they hold,
- * so that the append writes whole cache lines. Steps with prefill rows, cb_graph_step and
+ * (CB_SLOT_SOLE_WRITER). For such rows cb_step_forward (with the default "stage_kernel") and
+ * cb_graph_step rewrite the block's whole transposed V page, the other positions with the
+ * bits they hold, so that the append writes whole cache lines. Steps with prefill rows and
  * the copy-engine upload stage slots without the bit and write one element per d-row.
  * Returns CB_OK; the argument errors of cb_step_forward's host checks (CB_ERR_INVALID_ARG,
  * out-of-range block ids included); CB_ERR_UNSUPPORTED for pools beyond 2^31 / block_size

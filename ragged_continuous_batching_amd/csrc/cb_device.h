@@ -112,6 +112,9 @@ __device__ __forceinline__ void resolve_desc(AppendArgs& a) {
   a.ctx_lens = desc_array<const int32_t>(d, d->off_ctx);
   a.block_tables = desc_array<const int32_t>(d, d->off_bt);
   a.slots = d->off_slots ? desc_array<const int32_t>(d, d->off_slots) : nullptr;
+  a.n_marked = d->n_marked;
+  a.sole_bit = d->sole_bit;
+  a.marked = d->n_marked ? desc_array<const int32_t>(d, d->off_marked) : nullptr;
 }
 
 __device__ __forceinline__ void resolve_desc(RowArgs& a) {

@@ -63,8 +63,11 @@ struct StepDesc {
   int32_t n_prefill;            // prefill work-groups, empty launch-order slots included
   int64_t off_cu, off_ctx, off_bt, off_splits, off_combine, off_prefill, off_part_o, off_part_ml;
   int64_t off_slots;            // per-row cache slots (AppendArgs::slots); 0: none
+  int64_t off_marked;           // (row, slot) pairs of the marked rows (AppendArgs::marked)
+  int32_t n_marked, sole_bit;   // AppendArgs::n_marked and ::sole_bit
 };
 constexpr int kDescBytes = 256;        // the header's slot at the head of the workspace
+static_assert(sizeof(StepDesc) <= kDescBytes, "the step header must fit its slot");
 
 constexpr int kBlockSize = 16;         // KV positions per physical block
 constexpr int kPrefillKeys = 64;       // keys per prefill K/V tile (4 blocks)

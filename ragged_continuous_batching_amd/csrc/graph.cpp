@@ -75,9 +75,11 @@ void retire_pinned(void* p) {
 }
 
 // Byte layout of a replayed step: header, metadata, then the plan at plan_base (plan offsets
-// are relative to it). The stage copy moves [0, stage_bytes).
+// are relative to it). The stage copy moves [0, stage_bytes); the marked rows' (row, slot)
+// pairs follow in the pinned buffer only (pinned_bytes), read there by the append node.
 struct GraphLayout {
   size_t off_cu = 0, off_ctx = 0, off_bt = 0, off_slots = 0, plan_base = 0, stage_bytes = 0, total = 0;
+  size_t pinned_bytes = 0;
 };
 
 GraphLayout graph_layout(int32_t R, int64_t bt_entries, int32_t T, const Plan& p) {
@@ -88,6 +90,7 @@ GraphLayout graph_layout(int32_t R, int64_t bt_entries, int32_t T, const Plan& p
   l.off_slots = l.off_bt + static_cast<size_t>(bt_entries) * 4;
   l.plan_base = align256(l.off_slots + static_cast<size_t>(T) * 4);
   l.stage_bytes = (l.plan_base + p.plan_bytes + 15) & ~size_t{15};
+  l.pinned_bytes = l.stage_bytes + static_cast<size_t>(T) * 8;
   l.total = std::max(l.plan_base + p.total, l.stage_bytes);
   return l;
 }
@@ -143,7 +146,7 @@ int chain_nodes(hipGraph_t graph, std::vector<hipGraphNode_t>& out) {
 int graph_capture(cb_graph* g, const Plan& p, const GraphLayout& l) {
   graph_wait_all(g);
   g->captured = false;                      // until every slot holds a complete graph again
-  g->cap_stage = grow_size(l.stage_bytes, g->cap_stage);
+  g->cap_stage = grow_size(l.pinned_bytes, g->cap_stage);
   const size_t bytes = grow_size(std::max(l.total, g->cap_stage), g->ws_bytes);
   if (g->ws) hipFree(g->ws);
   g->ws = nullptr;
@@ -300,13 +303,14 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
                             "cb_graph_step")))
     return st;
   const bool slots = slots_fit(sh);           // with slots, the compact block table (as cb_step_forward)
+  const bool marks = slots && sole_marks_apply(sh, num_reqs, h_cu_q_lens);
   std::vector<int32_t> bt_rows;
   const int64_t nbt = slots ? compact_rows(num_reqs, h_cu_q_lens, h_ctx_lens, bt_rows)
                             : static_cast<int64_t>(num_reqs) * max_blocks_per_req;
   Plan p;
   make_plan(sh, &b, p, g->captured ? g->prefill_waves : 0, false, slots ? bt_rows.data() : nullptr);
   const GraphLayout l = graph_layout(num_reqs, nbt, num_tokens, p);
-  const bool fits = g->captured && l.stage_bytes <= g->cap_stage && l.total <= g->ws_bytes &&
+  const bool fits = g->captured && l.pinned_bytes <= g->cap_stage && l.total <= g->ws_bytes &&
                     p.mfma_decode == g->mfma_decode && p.group == g->group;
   if (!fits && (st = graph_capture(g, p, l))) return st;
 
@@ -315,6 +319,12 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
     if (hipEventSynchronize(sl.done) != hipSuccess) return fail(CB_ERR_HIP, "cb_graph_step: event wait failed");
     sl.in_flight = false;
   }
+  char* host = static_cast<char*>(sl.host);
+  int32_t n_marked = 0;
+  if (slots)
+    n_marked = fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
+                          reinterpret_cast<int32_t*>(host + l.off_slots), marks,
+                          marks ? reinterpret_cast<int32_t*>(host + l.stage_bytes) : nullptr);
   // live grids (a kind of work with no items keeps one work-group, which finds a zero count)
   const int32_t n_rows = static_cast<int32_t>(p.splits.size()) * sh->num_kv_heads * p.n_sub;
   const int32_t n_comb = static_cast<int32_t>(p.combine.size());
@@ -322,13 +332,13 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   const int64_t n16 = static_cast<int64_t>(l.stage_bytes / 16);
   auto blocks = [](int64_t n, int64_t per) { return static_cast<unsigned>(std::max<int64_t>(1, (n + per - 1) / per)); };
   if ((st = set_grid(sl, kNodeStage, dim3(std::min(blocks(n16, 256), 1024u)))) ||
-      (st = set_grid(sl, kNodeAppend, append_grid(num_tokens, sh->num_kv_heads, elem_bytes(sh), sh->head_dim))) ||
+      (st = set_grid(sl, kNodeAppend, append_grid(num_tokens, sh->num_kv_heads, elem_bytes(sh), sh->head_dim,
+                                                  n_marked))) ||
       (st = set_grid(sl, kNodePrefill, dim3(blocks(n_pre, 1)))) ||
       (st = set_grid(sl, kNodeDecode, dim3(blocks(n_rows, 4)))) ||
       (st = set_grid(sl, kNodeCombine, dim3(blocks(static_cast<int64_t>(n_comb) * sh->num_q_heads, 4)))))
     return st;
 
-  char* host = static_cast<char*>(sl.host);
   StepDesc d{};
   d.stage_bytes = static_cast<int64_t>(l.stage_bytes);
   d.num_reqs = num_reqs;
@@ -346,14 +356,15 @@ extern "C" int cb_graph_step(cb_graph* g, int32_t num_reqs, int32_t num_tokens, 
   d.off_part_o = static_cast<int64_t>(l.plan_base + p.off_part_o);
   d.off_part_ml = static_cast<int64_t>(l.plan_base + p.off_part_ml);
   d.off_slots = slots ? static_cast<int64_t>(l.off_slots) : 0;
+  d.off_marked = static_cast<int64_t>(l.stage_bytes);
+  d.n_marked = n_marked;
+  d.sole_bit = marks ? kSlotSoleWriter : 0;
   std::memcpy(host, &d, sizeof(d));
   std::memcpy(host + l.off_cu, h_cu_q_lens, static_cast<size_t>(num_reqs + 1) * 4);
   std::memcpy(host + l.off_ctx, h_ctx_lens, static_cast<size_t>(num_reqs) * 4);
   if (slots) {
     fill_compact(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables, bt_rows,
                  reinterpret_cast<int32_t*>(host + l.off_bt));
-    fill_slots(num_reqs, max_blocks_per_req, h_cu_q_lens, h_ctx_lens, h_block_tables,
-               reinterpret_cast<int32_t*>(host + l.off_slots), false);   // replays write V^T element-wise
   } else {
     std::memcpy(host + l.off_bt, h_block_tables, static_cast<size_t>(num_reqs) * max_blocks_per_req * 4);
   }

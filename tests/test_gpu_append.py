@@ -163,18 +163,19 @@ def check_cache_live(run, step):
     assert torch.equal(bits(run.v_cache[blk, :, :, off]), bits(run.gather(W.KIND_V, rids, pos)))
 
 
+@pytest.mark.parametrize("path", ["step_forward", "graph"])
 @pytest.mark.parametrize("with_chunk", [False, True])
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (6, 3)])
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
-def test_whole_page_rewrites_keep_every_other_slot(dtype, d, hq, hkv, with_chunk):
+def test_whole_page_rewrites_keep_every_other_slot(dtype, d, hq, hkv, with_chunk, path):
     """In a decode-only step, rows alone in their block rewrite its whole transposed V page
     (cb_step_slots marks them); the other positions of that page must come back with the
     bits they held (finite values, and NaN where nothing was written). A hand-built step:
     decode rows alone in their blocks at the first, middle and last slot, and two decode rows
     whose requests share one block (not marked: each writes its element). With a prefill
     chunk added, no row is marked and every row writes element by element. The whole cache is
-    compared bit for bit with the expected one. Odd kv head counts leave the last page
-    work-group of two heads (D = 64 in bf16) with one."""
+    compared bit for bit with the expected one, after cb_step_forward or a captured step.
+    Odd kv head counts leave the last page work-group of two heads (D = 64 in bf16) with one."""
     nb, bs = 48, 16
     shape = cb.make_shape(hq, hkv, d, nb, dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -214,10 +215,19 @@ def test_whole_page_rewrites_keep_every_other_slot(dtype, d, hq, hkv, with_chunk
     kc, vc = k_cache.cuda(), v_cache.cuda()
     qd, kd, vd = q.cuda(), k_new.cuda(), v_new.cuda()
     out = torch.empty_like(qd)
-    need = cb.cb_step_workspace_size(shape, len(reqs), T, maxb, cu, ctx)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    cb.cb_step_forward(shape, len(reqs), T, maxb, cu, ctx, bt, qd, kd, vd, kc, vc, d ** -0.5, out, ws, need,
-                       torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    if path == "step_forward":
+        need = cb.cb_step_workspace_size(shape, len(reqs), T, maxb, cu, ctx)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        cb.cb_step_forward(shape, len(reqs), T, maxb, cu, ctx, bt, qd, kd, vd, kc, vc, d ** -0.5, out, ws, need,
+                           stream)
+    else:
+        gr = cb.cb_graph_create(shape, T, qd, kd, vd, kc, vc, d ** -0.5, out)
+        try:
+            cb.cb_graph_step(gr, len(reqs), T, maxb, cu, ctx, bt, stream)
+            torch.cuda.synchronize()
+        finally:
+            cb.cb_graph_destroy(gr)
     torch.cuda.synchronize()
     assert torch.equal(bits(kc.cpu()), bits(k_exp))
     assert torch.equal(bits(vc.cpu()), bits(v_exp))
