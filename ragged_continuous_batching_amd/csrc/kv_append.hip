@@ -2,8 +2,9 @@
 //
 // zhangchitc "continuous-batching", section "Inside the kernel": once the QKV projection
 // has produced a step's keys and values, each row is stored in the cache slot of the
-// request it belongs to, and only then does attention read the cache. The cache is paged (fixed-size physical blocks,
-// hassanahmed "How continuous batching speeds up LLM serving", paged-memory section).
+// request it belongs to, and only then does attention read the cache. The cache is paged
+// (fixed-size physical blocks, hassanahmed "How continuous batching speeds up LLM serving",
+// paged-memory section).
 //
 // Layout (include/cb.h): K pages are [block_size][D], V pages are [D][block_size] (V is
 // stored transposed). A work-group takes 16 consecutive packed rows and one kv head (two at
@@ -20,13 +21,14 @@
 //   4. other rows (decode rows, the edges of a chunk) are written element by element, except
 //      rows the host marks as the only row of the step writing into their block (decode
 //      rows of a decode-only step): extra work-groups at the start of the grid, two marked
-//      rows each, rewrite those blocks' whole V^T pages. A page is read, the row's element put into
-//      each d-row, and every chunk stored back, the other slots with their own bits. One
-//      element per 32-byte d-row leaves partly written cache lines, which memory merges
-//      later at the cost of a read and a write each: skipping those writes altogether (a
-//      timing copy) took 12-13 us off a step of 64 decode rows x 32 kv heads or 256 x 8,
-//      most of it in the kernels after the append. A prefill kernel between the append and
-//      the decode rows hides that merge, so the host marks rows only in decode-only steps.
+//      rows each, rewrite those blocks' whole V^T pages. A page is read, the row's element
+//      put into each d-row, and every chunk stored back, the other slots with their own
+//      bits. One element per 32-byte d-row leaves partly written cache lines, which memory
+//      merges later at the cost of a read and a write each: skipping those writes
+//      altogether (a timing copy) took 12-13 us off a step of 64 decode rows x 32 kv heads
+//      or 256 x 8, most of it in the kernels after the append. A prefill kernel between the
+//      append and the decode rows hides that merge, so the host marks rows only in
+//      decode-only steps.
 #include <algorithm>
 #include <type_traits>
 
