@@ -204,6 +204,8 @@ def main(argv=None):
     ap.add_argument("--all-kernel-events", action="store_true",
                     help="config 5: an event pair around every kernel of the timed steps (default: only "
                          "around the launches that stream the cache)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip timing the paged read probe (the attainable rate reported beside HBM rooflines)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain elementwise copy of 512 MiB (read 512 MiB, write 512 MiB) three "
                          "times, so that counter runs can scale FETCH_SIZE/WRITE_SIZE by a known size")
@@ -235,6 +237,7 @@ def main(argv=None):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    rate = None if args.no_read_probe else paged_read_rate()
     if args.config == 5:
         result = bench_trace(args)
     elif args.config is not None or args.long_chunk:
@@ -248,8 +251,58 @@ def main(argv=None):
                 result["configs"][str(c)] = sub_result(bench_fixed(args, c, cpu_budget_s=5.0))
             release_device_memory()
             result["configs"]["5"] = sub_result(bench_trace(args, trace_window=True))
+    if rate is not None:
+        add_attainable(result, rate)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def paged_read_rate(n_pages=1 << 19, reps=5, per_rep=4):
+    """GB/s at which this GPU reads 4 KiB pages in a random order with the decode kernels'
+    loads (cb_paged_read_probe over 2 GiB, a seeded permutation). Each timed repetition is
+    `per_rep` back-to-back launches between two torch events, enqueued behind a launch that
+    keeps the GPU busy, so the host's launch overhead never shows as idle time between the
+    events; the best of `reps` repetitions after a warm-up."""
+    import torch
+
+    from ragged_continuous_batching_amd import cb
+    pages = torch.ones(n_pages * 4096, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    order = torch.randperm(n_pages, generator=g, device="cuda", dtype=torch.int32)
+    sink = torch.zeros(cb.cb_paged_read_probe_sink_words(n_pages), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def probe():
+        cb.cb_paged_read_probe(pages, n_pages, order, sink, stream.cuda_stream)
+
+    best = float("inf")
+    for i in range(reps + 1):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        probe()                                   # keeps the GPU busy while the rest is enqueued
+        t0.record(stream)
+        for _ in range(per_rep):
+            probe()
+        t1.record(stream)
+        t1.synchronize()
+        if i >= 1:
+            best = min(best, t0.elapsed_time(t1) / per_rep)
+    del pages, order, sink
+    release_device_memory()
+    return n_pages * 4096 / (best * 1e-3) / 1e9
+
+
+def add_attainable(result, rate):
+    """Puts the decode kernels' bandwidth beside the probe's paged read rate."""
+    for r in [result] + list(result.get("configs", {}).values()):
+        roof = r.get("roofline")
+        if isinstance(roof, dict) and roof.get("bound") == "hbm" and roof.get("achieved"):
+            roof["attainable"] = round(rate, 1)
+            roof["frac_of_attainable"] = round(roof["achieved"] / rate, 4)
+    result["attainable_read"] = {"value": round(rate, 1), "unit": "GB/s",
+                                 "probe": "cb_paged_read_probe: 2 GiB of 4 KiB pages in a seeded random order, "
+                                          "non-temporal 16-byte loads as the decode kernels issue them; best of 5 "
+                                          "repetitions of 4 back-to-back launches"}
 
 
 def release_device_memory():

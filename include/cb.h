@@ -360,6 +360,20 @@ int cb_profile_reset(void);
 int cb_profile_select(uint32_t mask);
 const char* cb_kernel_name(int kernel_id);
 
+/* A measurement aid, not part of a step: reads n_pages 4 KiB pages of `pages` in the order
+ * `order` the way the decode kernels read the cache (non-temporal 16-byte loads of whole
+ * pages; each wave requests its 16 pages before it uses the first) and does nothing with them. Timed around its launch,
+ * it gives the read rate this GPU attains on the cache's access pattern; bench.py reports
+ * the decode kernels against it beside the vendor figure.
+ *   pages  device, n_pages * 4096 bytes, 16-byte aligned
+ *   order  device int32 [n_pages], page indices (entries outside [0, n_pages) are skipped)
+ *   sink   device uint32 [cb_paged_read_probe_sink_words(n_pages)], practically never written
+ * Asynchronous on `stream`. Returns CB_OK, or CB_ERR_INVALID_ARG for n_pages < 1, a NULL or
+ * misaligned pointer. */
+int32_t cb_paged_read_probe_sink_words(int32_t n_pages);
+int cb_paged_read_probe(const void* pages, int32_t n_pages, const int32_t* order, uint32_t* sink,
+                        void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Host step builder (Hugging Face blog, section "Continuous batching": aim for m tokens per
  * step, add every decoding request first with one token each, fill the rest with prefill

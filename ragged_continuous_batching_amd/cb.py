@@ -104,6 +104,8 @@ def _load():
         "cb_profile_reset": (ctypes.c_int, []),
         "cb_profile_select": (ctypes.c_int, [ctypes.c_uint32]),
         "cb_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+        "cb_paged_read_probe_sink_words": (ctypes.c_int32, [ctypes.c_int32]),
+        "cb_paged_read_probe": (ctypes.c_int, [P, ctypes.c_int32, P, P, P]),
         "cb_sched_create": (P, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]),
         "cb_sched_add": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
         "cb_sched_set_static": (ctypes.c_int, [P, ctypes.c_int32]),
@@ -135,7 +137,7 @@ EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_plan_descr
             "cb_step_forward", "cb_step_slots", "cb_last_error",
             "cb_version", "cb_set_tuning", "cb_get_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
             "cb_profile_reset", "cb_profile_select",
-            "cb_kernel_name", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
+            "cb_kernel_name", "cb_paged_read_probe_sink_words", "cb_paged_read_probe", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
             "cb_sched_set_preemption", "cb_linear", "cb_qkv_project", "cb_graph_create", "cb_graph_step",
             "cb_graph_stats", "cb_graph_destroy")
@@ -354,6 +356,16 @@ def cb_profile_reset() -> int:
 
 def cb_kernel_name(kernel_id: int) -> str:
     return lib.cb_kernel_name(int(kernel_id)).decode()
+
+
+def cb_paged_read_probe_sink_words(n_pages: int) -> int:
+    return int(lib.cb_paged_read_probe_sink_words(int(n_pages)))
+
+
+def cb_paged_read_probe(pages, n_pages: int, order, sink, stream=None) -> int:
+    """Reads n_pages 4 KiB pages in the given order as the decode kernels read the cache
+    (a measurement aid; device tensors in, nothing out)."""
+    return _check(lib.cb_paged_read_probe(_ptr(pages), int(n_pages), _ptr(order), _ptr(sink), _stream(stream)))
 
 
 # ---- host step builder ----------------------------------------------------------------

@@ -568,6 +568,17 @@ extern "C" int cb_step_forward(const cb_shape* shape, int32_t num_reqs, int32_t 
 
 static_assert(kSlotSoleWriter == CB_SLOT_SOLE_WRITER, "the staged sole-writer bit is the one cb.h documents");
 
+extern "C" int32_t cb_paged_read_probe_sink_words(int32_t n_pages) { return n_pages > 0 ? paged_read_grid(n_pages) : 0; }
+
+extern "C" int cb_paged_read_probe(const void* pages, int32_t n_pages, const int32_t* order, uint32_t* sink,
+                                   void* stream) {
+  if (n_pages < 1 || !pages || !order || !sink || !aligned16(pages))
+    return fail(CB_ERR_INVALID_ARG, "cb_paged_read_probe: needs n_pages >= 1 and non-NULL pointers, pages 16-byte aligned");
+  const hipError_t e = launch_paged_read(pages, n_pages, order, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_paged_read_probe: launch failed: %s", hipGetErrorString(e));
+  return CB_OK;
+}
+
 extern "C" int cb_step_slots(const cb_shape* shape, int32_t num_reqs, int32_t num_tokens, int32_t max_blocks_per_req,
                              const int32_t* h_cu_q_lens, const int32_t* h_ctx_lens, const int32_t* h_block_tables,
                              int32_t* out_slots) {

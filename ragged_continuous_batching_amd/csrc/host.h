@@ -19,6 +19,10 @@ hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int head_dim, h
 // Grid of kv_append_kernel for num_tokens rows (256-thread work-groups); launch_kv_append and
 // the captured step both take it from here.
 dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int head_dim, int32_t n_marked = 0);
+// The paged-read probe (probe.hip): work-groups for n_pages, and its launch.
+int32_t paged_read_grid(int32_t n_pages);
+hipError_t launch_paged_read(const void* pages, int32_t n_pages, const int32_t* order, uint32_t* sink,
+                             hipStream_t s);
 hipError_t launch_rows(const RowArgs& a, int elem_bytes, int head_dim, int group, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int waves, hipStream_t s);

@@ -270,3 +270,18 @@ def test_noalloc_rejects_a_plan_larger_than_its_array():
     assert st == cb.CB_ERR_WORKSPACE_TOO_SMALL
     assert "fixed" in cb.cb_last_error()
     assert "CB_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
+
+
+def test_paged_read_probe_checks_arguments():
+    """The measurement probe rejects an empty or NULL page set before any launch, and sizes
+    its sink at one word per work-group of 64 pages."""
+    assert cb.cb_paged_read_probe_sink_words(0) == 0
+    assert cb.cb_paged_read_probe_sink_words(1) == 1
+    assert cb.cb_paged_read_probe_sink_words(64) == 1
+    assert cb.cb_paged_read_probe_sink_words(65) == 2
+    with pytest.raises(cb.CbError):
+        cb.cb_paged_read_probe(None, 16, None, None)
+    with pytest.raises(cb.CbError):
+        cb.cb_paged_read_probe(256, 0, 256, 256)
+    with pytest.raises(cb.CbError):          # misaligned pages
+        cb.cb_paged_read_probe(257, 4, 256, 256)

@@ -787,3 +787,17 @@ def test_decode_rows_longest_first_order(hq, hkv):
         cb.cb_set_tuning("decode_order", 1)
     assert torch.equal(outs[0], outs[1])
     check(outs[1], oracle_full(wl, step), "bf16", f"decode rows-first order Hq={hq} Hkv={hkv}")
+
+
+def test_paged_read_probe_runs_and_writes_nothing():
+    """The bench's measurement probe reads every page it is given (entries outside the pool
+    skipped) and leaves its sink alone: constant pages fold to zero, never the sink's key."""
+    n = 1000
+    pages = torch.full((n * 4096,), 3, dtype=torch.uint8, device="cuda")
+    order = torch.randperm(n, device="cuda", dtype=torch.int32)
+    order[7] = n + 5                                  # skipped
+    order[11] = -1                                    # skipped
+    sink = torch.zeros(cb.cb_paged_read_probe_sink_words(n), dtype=torch.int32, device="cuda")
+    cb.cb_paged_read_probe(pages, n, order, sink, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum().item()) == 0
