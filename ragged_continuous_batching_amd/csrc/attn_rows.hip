@@ -209,15 +209,29 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
     wave_fence();
   };
 
+  // Two blocks in flight. In the steady-state loop every load is issued on every path, so the
+  // compiler's wait before each block's first use counts exactly the loads issued after it:
+  // loads issued only on some paths (the split's last blocks) would make it wait, on every
+  // path, as if they were never issued, draining the next block's loads before this one's
+  // dot products start. A split of one block reads it twice (its second load is never used).
   u32x4 kA[NLK], vA[NLV], kB[NLK], vB[NLV];
   const int b0 = sp.blk_begin, b1 = sp.blk_end;
   load_block(b0, kA, vA);
-  for (int b = b0; b < b1; b += 2) {
-    if (b + 1 < b1) load_block(b + 1, kB, vB);
+  load_block(min(b0 + 1, b1 - 1), kB, vB);
+  int b = b0;
+  for (; b + 3 < b1; b += 2) {
     process(b, kA, vA);
-    if (b + 2 < b1) load_block(b + 2, kA, vA);
-    if (b + 1 < b1) process(b + 1, kB, vB);
+    __builtin_amdgcn_sched_barrier(0);     // the next loads reuse this block's registers
+    load_block(b + 2, kA, vA);
+    process(b + 1, kB, vB);
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(b + 3, kB, vB);
   }
+  // the last one to three blocks
+  process(b, kA, vA);
+  if (b + 2 < b1) load_block(b + 2, kA, vA);
+  if (b + 1 < b1) process(b + 1, kB, vB);
+  if (b + 2 < b1) process(b + 2, kA, vA);
 
   // reduce over the VL lanes that share a d-row, and the sums over key-row groups
   const bool writer = (lane % VL) == 0;
