@@ -36,13 +36,18 @@
 
 namespace cb {
 
+// Packed rows per work-group. More rows per work-group (fewer, longer work-groups) measured
+// slower: config 2's append 21.7 -> 24.7 us at 32 or 64 rows, the chunked-prefill-heavy step's
+// 50.5 -> 59.5-61.5 us (the trace's steps 24.1 -> 23.4-23.8 us).
+constexpr int kAppendRows = 16;
+
 // kv heads per work-group: as few as give every thread a whole number of 16-byte chunks
 // (one head at D = 128 in bf16). More, smaller work-groups finish the scattered V^T stores
 // sooner: one head instead of four measured 17.3 -> 12.4 us on 256 decode rows (Hkv = 8)
 // and 22.3 -> 18.2 us on a 2048-row mixed step (Hkv = 32).
 template <int ES, int D>
 constexpr int append_heads() {
-  return 256 / (16 * (D * ES / 16)) > 1 ? 256 / (16 * (D * ES / 16)) : 1;
+  return 256 / (kAppendRows * (D * ES / 16)) > 1 ? 256 / (kAppendRows * (D * ES / 16)) : 1;
 }
 
 // Whole V^T pages of marked rows m0 .. m0 + kPageRows - 1, kv heads g0 .. g0 + nheads - 1.
@@ -100,13 +105,14 @@ template <int ES, int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   constexpr int VEC = 16 / ES;              // elements per 16-byte chunk
   constexpr int CH = D / VEC;               // chunks per row
-  constexpr int ROWS = 16, HEADS = append_heads<ES, D>();
+  constexpr int ROWS = kAppendRows, HEADS = append_heads<ES, D>();
+  static_assert(ROWS <= 64, "the marked rows of a work-group are one 64-bit mask");
   constexpr int LS = D + 16 / ES;           // LDS row stride (elements): spreads banks
   using E = typename std::conditional<ES == 2, uint16_t, uint32_t>::type;
   __shared__ __align__(16) E vt[HEADS * ROWS * LS];
   __shared__ int32_t info_blk[ROWS], info_off[ROWS];
   __shared__ int32_t info_run[ROWS / VEC];
-  __shared__ uint32_t info_sole;               // bit r: row r rewrites its whole V^T page
+  __shared__ uint64_t info_sole;               // bit r: row r rewrites its whole V^T page
 
   if (a.desc) resolve_desc(a);
   // The page work-groups come first, so that their longer chains (pinned list, page, stores)
@@ -174,8 +180,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     }
     info_blk[tid] = blk;
     info_off[tid] = off;
-    const uint64_t sole_rows = __ballot(sole && blk >= 0);   // the 16 lanes of wave 0
-    if (tid == 0) info_sole = static_cast<uint32_t>(sole_rows);
+    const uint64_t sole_rows = __ballot(sole && blk >= 0);   // the first ROWS lanes of wave 0
+    if (tid == 0) info_sole = sole_rows;
   }
   // V rows into LDS
 #pragma unroll
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     } else {
       for (int i = 0; i < VEC && r0 + i < nrows; ++i) {
         const int blk = info_blk[r0 + i];
-        if (blk < 0 || ((info_sole >> (r0 + i)) & 1u)) continue;
+        if (blk < 0 || ((info_sole >> (r0 + i)) & 1u) != 0) continue;
         const int64_t page = static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh;
         static_cast<E*>(a.v_cache)[(page * D + d) * kBlockSize + info_off[r0 + i]] = src[i * LS];
       }
@@ -241,7 +247,7 @@ dim3 append_grid(int64_t num_tokens, int32_t num_kv_heads, int elem_bytes, int h
                                 : (head_dim == 128 ? append_heads<4, 128>() : append_heads<4, 64>());
   // at least one work-group in each dimension (a captured step may replay with no rows; the
   // kernel exits for rows and heads past the end); the page work-groups follow the rows'
-  const int64_t x = (num_tokens + 15) / 16 + (std::max(n_marked, 0) + kPageRows - 1) / kPageRows,
+  const int64_t x = (num_tokens + kAppendRows - 1) / kAppendRows + (std::max(n_marked, 0) + kPageRows - 1) / kPageRows,
                 y = (num_kv_heads + h - 1) / h;
   return dim3(static_cast<unsigned>(x > 0 ? x : 1), static_cast<unsigned>(y > 0 ? y : 1));
 }
