@@ -16,6 +16,8 @@
 // token and four consecutive features per accumulator group: row-major stores (C, Q, K
 // pages) are 8-byte vectors, and the transposed V pages get one element per lane with
 // consecutive lanes on consecutive positions.
+#include <type_traits>
+
 #include "cb_device.h"
 
 namespace cb {
@@ -148,8 +150,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bt_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tn][tm][i] = 0.f;
 
-  auto step = [&](int ks, int set) {             // set = ks % 2
-    if (ks + 2 < nk) load(ks + 2, set);
+  // FULL: the step issues its loads unconditionally (the steady state), so the compiler's wait
+  // before each register set is stored counts exactly the loads issued after it; a load
+  // issued on some paths only makes it wait, on every path, as if it were never issued,
+  // draining the loads for two steps ahead before the store of the next tile.
+  auto step = [&](int ks, int set, auto full) {  // set = ks % 2
+    if (decltype(full)::value || ks + 2 < nk) load(ks + 2, set);
+    __builtin_amdgcn_sched_barrier(0);           // the loads go out before the step's products
     const uint16_t* la = lds + set * (TA + TB);
     const uint16_t* lb = la + TA;
 #pragma unroll
@@ -176,14 +183,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bt_kernel(GemmArgs g) {
     if (ks + 1 < nk) store(set ^ 1, set ^ 1);   // tile ks+1: LDS buffer and register set (ks+1)%2
     __syncthreads();
   };
+  // (a K of one step also loads step 1, which its buffer resources read as zeros or as
+  // bytes never used)
   load(0, 0);
-  if (nk > 1) load(1, 1);
+  load(1, 1);
   store(0, 0);
   __syncthreads();
-  for (int ks = 0; ks < nk; ks += 2) {
-    step(ks, 0);
-    if (ks + 1 < nk) step(ks + 1, 1);
+  int ks = 0;
+  for (; ks + 3 < nk; ks += 2) {
+    step(ks, 0, std::true_type{});
+    step(ks + 1, 1, std::true_type{});
   }
+  for (; ks < nk; ++ks) step(ks, ks & 1, std::false_type{});
 
   // epilogue: lane owns token m0 + wm*64 + tm*32 + col and, per group q4 of accumulator
   // elements, features n0 + wn*BN/2 + tn*32 + 8*q4 + 4*grp + (0..3)
