@@ -27,7 +27,8 @@
 //
 // Key and value tiles go from the cache straight into LDS (buffer_load_dwordx4 ... lds: no
 // staging registers and no LDS store instructions) through two K buffers and two V
-// buffers. Tile t's keys are first read one step before its values (the scores of tile t
+// buffers; in an eight-wave work-group only waves 0-3 issue them (see the direct loads).
+// Tile t's keys are first read one step before its values (the scores of tile t
 // are computed while tile t-1's probabilities are applied), so K(t+3) and V(t+2) are
 // requested right after the barrier that ends step t, and waited for at the end of step
 // t+1: one barrier per tile.
@@ -126,36 +127,43 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     }
   }
 
-  // Direct loads: a tile is 4 * IPP 1-KB pieces of keys and as many of values; wave w takes
-  // pieces w*LPW .. w*LPW+LPW-1, which all lie in page pw of the tile. Each lane's source
-  // offset inside its cache page is fixed; only the page's block id changes from tile to
-  // tile (one id per wave and tile, the same in every lane).
-  constexpr int LPW = 4 * IPP / NW;                                // pieces per wave per tile
-  static_assert(LPW >= 1 && LPW * NW == 4 * IPP, "pieces must divide evenly over the waves");
-  const int pw = wave * LPW / IPP;                                 // page of this wave's pieces
-  // piece u of this wave: its place in the page, and its LDS offset in a buffer (wave-uniform,
-  // recomputed where used rather than kept in scalar registers through the loop)
-  auto piece = [&](int u) { return (wave * LPW + u) % IPP; };
-  auto piece_lds = [&](int u) { return static_cast<uint32_t>(pw * PAGE + piece(u) * 1024); };
-  uint32_t ksrc[LPW], vsrc[LPW];
+  // Direct loads: a tile is four cache pages of keys and four of values, each page IPP 1-KB
+  // pieces. Only waves 0-3 load: loading wave w takes page w of every tile, its IPP pieces of
+  // keys and of values. Each lane's source offset inside its cache page is fixed; only the
+  // page's block id changes from tile to tile (one id per wave and tile, the same in every
+  // lane). A CU's load path moves about 64 bytes per clock, so a tile's 32 KB keep it busy
+  // for about 512 clocks, and a wave that issues a load waits until the path takes it. In an
+  // eight-wave work-group waves w and w+4 share a SIMD, so while the loading wave of a SIMD
+  // waits, its partner keeps the matrix core busy (config 4 measured 3409 -> 3136 clocks per
+  // key tile and wave; when all eight waves loaded, both waves of a SIMD waited together).
+  // Four-wave work-groups have one wave per SIMD, and every wave loads.
+  constexpr int NL = 4;                                            // waves that load tiles
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  const bool loader = wave < NL;
+  const int pw = wave;                                             // page of a loading wave
+  // LDS offset of this wave's page in a buffer. Made opaque where it is used, so the
+  // compiler computes each piece's LDS address at its load instead of keeping all of them in
+  // scalar registers through the loop (which spilled them into vector-register lanes).
+  auto page_lds = [&]() {
+    int o = pw * PAGE;
+    asm volatile("" : "+s"(o));
+    return static_cast<uint32_t>(o);
+  };
+  uint32_t ksrc[IPP], vsrc[IPP];
 #pragma unroll
-  for (int u = 0; u < LPW; ++u) {
-    const int part = piece(u);
+  for (int part = 0; part < IPP; ++part) {
     // keys: chunks 4*part .. 4*part+3 of positions 0..15 (lane: chunk 4*part + lane/16,
     // position lane%16)
-    ksrc[u] = (lane % 16) * (2 * D) + (4 * part + lane / 16) * 16;
+    ksrc[part] = (lane % 16) * (2 * D) + (4 * part + lane / 16) * 16;
     // values: d-rows 32*part .. +31 (lane: row 32*part + lane/2, stored half lane%2)
     const int d = 32 * part + lane / 2;
-    vsrc[u] = d * 32 + ((lane & 1) ^ ((d >> 3) & 1)) * 16;
+    vsrc[part] = d * 32 + ((lane & 1) ^ ((d >> 3) & 1)) * 16;
   }
   // Block id of key page pidx (clamped to the last page the work-group sees; ids outside the
   // pool read block 0). The index is wave-uniform.
   const int last_page = __builtin_amdgcn_readfirstlane((wg_keys - 1) / kBlockSize);
   auto page_of = [&](int t) { return min((kt0 + t) * 4 + pw, last_page); };   // this wave's page of tile t
   auto valid_block = [&](int blk) { return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0; };
-  auto block_scalar = [&](int t) {
-    return valid_block(__builtin_amdgcn_readfirstlane(__builtin_nontemporal_load(bt + page_of(t))));
-  };
   // a buffer resource over one cache page (its byte range bounds the lanes' offsets)
   auto page_rsrc = [&](const uint8_t* cache, int blk) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache + (static_cast<int64_t>(blk) * hkv + g) * PAGE),
@@ -163,29 +171,31 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   };
   auto load_k = [&](uint8_t* dst, int blk) {
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(kc, blk);
+    const uint32_t base = page_lds();
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) load_to_lds(rs, ksrc[u], dst + piece_lds(u));
+    for (int part = 0; part < IPP; ++part) load_to_lds(rs, ksrc[part], dst + base + part * 1024);
   };
   auto load_v = [&](uint8_t* dst, int blk) {
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(vc, blk);
+    const uint32_t base = page_lds();
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) load_to_lds(rs, vsrc[u], dst + piece_lds(u));
+    for (int part = 0; part < IPP; ++part) load_to_lds(rs, vsrc[part], dst + base + part * 1024);
   };
   // The tile that reaches wg_keys (the last key any row of this work-group sees): value
   // positions at or past it may hold anything (stale slots of the last page, or pages past
   // it, clamped to it), and a zero probability times a non-finite value is not zero, so each
-  // lane zeroes them in the 16-byte pieces it loaded itself (after its own loads landed).
+  // lane of a loading wave zeroes them in the 16-byte pieces it loaded itself (after its own
+  // loads landed).
   auto zero_tail = [&](uint8_t* vbuf, int t) {
     const int lim = wg_keys - (kt0 + t) * kPrefillKeys;            // valid positions of the tile
     if (lim >= kPrefillKeys) return;
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) {
-      const int part = piece(u);
+    for (int part = 0; part < IPP; ++part) {
       const int d = 32 * part + lane / 2;
       const int hf = (lane & 1) ^ ((d >> 3) & 1);                  // half of the page held here
       const int k0 = pw * kBlockSize + hf * 8;                     // its first position in the tile
       if (k0 + 8 > lim) {
-        u32x4* q = reinterpret_cast<u32x4*>(vbuf + piece_lds(u) + lane * 16);
+        u32x4* q = reinterpret_cast<u32x4*>(vbuf + pw * PAGE + part * 1024 + lane * 16);
         u32x4 v = *q;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
@@ -337,12 +347,19 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   };
 
   // prologue: keys of tiles 0 and 1 and values of tile 0 in LDS, the scores of tile 0, then
-  // the values of tile 1 and keys of tile 2 requested
-  load_k(kb0, block_scalar(0));
-  load_v(vb0, block_scalar(0));
-  if (n_tiles > 1) load_k(kb1, block_scalar(1));
+  // the values of tile 1 and keys of tile 2 requested. The block ids of the item's first 64
+  // pages come in one load, one per lane, so the first three tiles wait for one id load
+  // rather than one each.
+  const int ids0 = __builtin_nontemporal_load(bt + min(kt0 * 4 + lane, last_page));
+  auto first_block = [&](int t) { return valid_block(__builtin_amdgcn_readlane(ids0, t * 4 + pw)); };
+  if (loader) {
+    const int b0 = first_block(0);
+    load_k(kb0, b0);
+    load_v(vb0, b0);
+    if (n_tiles > 1) load_k(kb1, first_block(1));
+  }
   wait_vmem();
-  if (n_tiles == 1) zero_tail(vb0, 0);
+  if (loader && n_tiles == 1) zero_tail(vb0, 0);
   __syncthreads();
   f32x16 sa[2], sb[2];
   float mx = 0.f;                                // unmasked row max of the next tile's scores
@@ -351,9 +368,11 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
     mx = tile_max(sa);
   }
   __syncthreads();                               // K buffer 0 is read: it takes tile 2
-  if (n_tiles > 1) load_v(vb1, block_scalar(1));
-  if (n_tiles > 2) load_k(kb0, block_scalar(2));
-  fetch_ids(2, 3);
+  if (loader) {
+    if (n_tiles > 1) load_v(vb1, first_block(1));
+    if (n_tiles > 2) load_k(kb0, first_block(2));
+    fetch_ids(2, 3);
+  }
   // After step u (values of tile u in V buffer u&1, keys of tile u+1 in K buffer (u+1)&1):
   // wait for the requests of the previous barrier (values u+1, keys u+2, block ids), zero
   // the last tile's value tail, barrier (both buffers of step u are free), then request
@@ -361,13 +380,15 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   // the tiles after them.
   auto advance = [&](int u, uint8_t* vfree, uint8_t* kfree, uint8_t* vnext) {
     wait_vmem();
-    if (u + 1 == n_tiles - 1) zero_tail(vnext, u + 1);
+    if (loader && u + 1 == n_tiles - 1) zero_tail(vnext, u + 1);
     __syncthreads();
-    const int blk_v = valid_block(__builtin_amdgcn_readfirstlane(id_v));
-    const int blk_k = valid_block(__builtin_amdgcn_readfirstlane(id_k));
-    if (u + 2 < n_tiles) load_v(vfree, blk_v);
-    if (u + 3 < n_tiles) load_k(kfree, blk_k);
-    fetch_ids(u + 3, u + 4);
+    if (loader) {
+      const int blk_v = valid_block(__builtin_amdgcn_readfirstlane(id_v));
+      const int blk_k = valid_block(__builtin_amdgcn_readfirstlane(id_k));
+      if (u + 2 < n_tiles) load_v(vfree, blk_v);
+      if (u + 3 < n_tiles) load_k(kfree, blk_k);
+      fetch_ids(u + 3, u + 4);
+    }
   };
   int u = 0;
   for (; u + 1 < n_tiles; u += 2) {
