@@ -264,8 +264,17 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   // overlap within the wave. Only tiles that cross the causal diagonal need a mask (every key
   // of another tile is visible to every row of the wave), and only those recompute the max
   // after it.
+  // Lazy rescaling: the reference max only moves when some lane's max grew by more than
+  // 8 (log2 units). Until then probabilities may reach 2^8, which fp32 sums and bf16 P
+  // hold as well as values below 1; O and l share the reference, so O / l is unchanged.
+  // The scale is positive, so max(scale*s) = scale*max(s) and it folds into the fma.
+  // The test for a tile is made as soon as its row max is known (at the end of the step
+  // before, beside the last MFMAs), so the step itself starts with a scalar branch.
+  auto rescale_due = [&](float m) -> bool {
+    return __builtin_amdgcn_ballot_w64(fmaxf(m_run, m * a.scale_log2) > m_run + 8.f) != 0;
+  };
   auto tile_step = [&](int u, const uint8_t* vbuf, const uint8_t* knext, f32x16 (&s_cur)[2],
-                       f32x16 (&s_next)[2], float& mx) {
+                       f32x16 (&s_next)[2], float& mx, bool& resc) {
     const int j = kt0 + u;                       // absolute tile: positions and masks
     if (!wave_active || j * kPrefillKeys >= wave_keys) return;
     const bool diag = j * kPrefillKeys + kPrefillKeys - 1 > c + wave_row0;   // uniform (scalar) values
@@ -277,13 +286,10 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
         for (int i = 0; i < 16; ++i)
           if (kt * 32 + (i >> 3) * 16 + ((i >> 2) & 1) * 4 + (i & 3) > rel) s_cur[kt][i] = -INFINITY;
       mx = tile_max(s_cur);
+      resc = rescale_due(mx);
     }
-    // Lazy rescaling: the reference max only moves when some lane's max grew by more than
-    // 8 (log2 units). Until then probabilities may reach 2^8, which fp32 sums and bf16 P
-    // hold as well as values below 1; O and l share the reference, so O / l is unchanged.
-    // The scale is positive, so max(scale*s) = scale*max(s) and it folds into the fma.
-    const float m_cand = fmaxf(m_run, mx * a.scale_log2);
-    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + 8.f) != 0) {   // wave-uniform: a scalar branch
+    if (resc) {                                  // wave-uniform: a scalar branch
+      const float m_cand = fmaxf(m_run, mx * a.scale_log2);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
       m_run = m_cand;
       l_run *= alpha;
@@ -321,6 +327,7 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
         oacc[dt] = mfma32(va, pb[ks], oacc[dt]);
       }
     mx = tile_max(s_next);
+    resc = rescale_due(mx);
     // Instruction order for the block above (scheduler groups): each of its 32 MFMAs (the
     // next tile's scores, and the P.V products as soon as their quarter of P is packed)
     // is followed by an LDS operand read, issued four MFMAs ahead of its use, and three
@@ -363,9 +370,11 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   __syncthreads();
   f32x16 sa[2], sb[2];
   float mx = 0.f;                                // unmasked row max of the next tile's scores
+  bool resc = false;                             // its rescale test (lanes of the whole wave)
   if (wave_active) {
     compute_s(kb0, sa);
     mx = tile_max(sa);
+    resc = rescale_due(mx);
   }
   __syncthreads();                               // K buffer 0 is read: it takes tile 2
   if (loader) {
@@ -392,12 +401,12 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   };
   int u = 0;
   for (; u + 1 < n_tiles; u += 2) {
-    tile_step(u, vb0, kb1, sa, sb, mx);
+    tile_step(u, vb0, kb1, sa, sb, mx, resc);
     advance(u, vb0, kb1, vb1);
-    tile_step(u + 1, vb1, kb0, sb, sa, mx);
+    tile_step(u + 1, vb1, kb0, sb, sa, mx, resc);
     if (u + 2 < n_tiles) advance(u + 1, vb1, kb0, vb0);
   }
-  if (u < n_tiles) tile_step(u, vb0, kb1, sa, sb, mx);
+  if (u < n_tiles) tile_step(u, vb0, kb1, sa, sb, mx, resc);
 
   if (!wave_active) return;
   const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
