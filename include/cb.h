@@ -288,6 +288,19 @@ const char* cb_last_error(void);
 /* Library version string, e.g. "cb 0.1 gfx950". */
 const char* cb_version(void);
 
+/* Device checks of the debug copy of the library (python -m ragged_continuous_batching_amd.build
+ * --device-checks, loaded in place of libcb.so). The host checks a step's block ids against
+ * the pool from its host mirrors before it launches anything; the kernels read the device
+ * block table (and, for cb_step_forward, the staged slots). A kernel that meets a block id
+ * outside the pool (a device table that disagrees with its host mirror) reads block 0 in its
+ * place or skips the write, in every build, so it never faults; the debug copy also counts
+ * each such meeting (once per wave or work-group that meets it).
+ *   count  out: the count since the last reset, summed over every kernel (waits for the device)
+ *   reset  nonzero: zero the counters after reading them
+ * Returns CB_OK, or CB_ERR_UNSUPPORTED in a copy built without the checks (count is then 0).
+ * Not for use while other threads launch library work. */
+int cb_debug_violations(uint32_t* count, int reset);
+
 /* Tuning knobs (process-wide, host-side, read by every later call when it plans its launches;
  * a captured cb_graph keeps the kernels it was captured with). Set them before issuing work:
  * changing a knob while another thread is inside a library call is a data race. Keys:

@@ -6,6 +6,10 @@ Every HIP translation unit is compiled with packed-fp32 instruction selection di
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the hand-written kernels use no
 packed fp32 arithmetic either. Host-only sources (``*.cpp``) are compiled as C++.
 
+``--device-checks`` builds a debug copy, ``_build/checks/libcb.so``, whose kernels also count
+every block id outside the pool that they meet (they read block 0 in its place, as every
+build does); ``cb_debug_violations`` returns the count (tests/test_gpu_device_checks.py).
+
 ``--sanitize`` builds a test copy, ``_build/asan/libcb.so``, whose host code (the step
 builder, the planner, argument checks, the entry points) carries AddressSanitizer and
 UndefinedBehaviorSanitizer checks; device code is built as usual (each ``-fsanitize=``
@@ -30,6 +34,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcb.so")
 ASAN_BUILD = os.path.join(BUILD, "asan")
 ASAN_LIB = os.path.join(ASAN_BUILD, "libcb.so")
+CHECKS_BUILD = os.path.join(BUILD, "checks")
+CHECKS_LIB = os.path.join(CHECKS_BUILD, "libcb.so")
 # host-side sanitizers; every flag behind -Xarch_host so device code is not instrumented
 SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
@@ -61,9 +67,13 @@ def compile_one(src: str, out_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False, sanitize: bool = False) -> str:
-    out_dir, lib = (ASAN_BUILD, ASAN_LIB) if sanitize else (BUILD, LIB)
-    extra = SANITIZE if sanitize else []
+def build(jobs: int = 8, verbose: bool = False, sanitize: bool = False, device_checks: bool = False) -> str:
+    if sanitize:
+        out_dir, lib, extra = ASAN_BUILD, ASAN_LIB, SANITIZE
+    elif device_checks:
+        out_dir, lib, extra = CHECKS_BUILD, CHECKS_LIB, ["-DCB_DEVICE_CHECKS"]
+    else:
+        out_dir, lib, extra = BUILD, LIB, []
     os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
@@ -97,8 +107,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--sanitize", action="store_true", help="the host-sanitized test copy in _build/asan")
+    ap.add_argument("--device-checks", action="store_true", help="the debug copy with device checks in _build/checks")
     args = ap.parse_args(argv)
-    build(args.j, verbose=True, sanitize=args.sanitize)
+    build(args.j, verbose=True, sanitize=args.sanitize, device_checks=args.device_checks)
 
 
 if __name__ == "__main__":

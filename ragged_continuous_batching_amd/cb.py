@@ -93,6 +93,7 @@ def _load():
                                          P, P, P, P]),
         "cb_last_error": (ctypes.c_char_p, []),
         "cb_version": (ctypes.c_char_p, []),
+        "cb_debug_violations": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]),
         "cb_set_tuning": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
         "cb_get_tuning": (ctypes.c_int, [ctypes.c_char_p, _i32p]),
         "cb_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -135,7 +136,7 @@ EXPORTED = ("cb_kv_append", "cb_ragged_attention_workspace_size", "cb_plan_descr
             "cb_ragged_attention_noalloc",
             "cb_step_workspace_size",
             "cb_step_forward", "cb_step_slots", "cb_last_error",
-            "cb_version", "cb_set_tuning", "cb_get_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
+            "cb_version", "cb_debug_violations", "cb_set_tuning", "cb_get_tuning", "cb_profile_enable", "cb_profile_read", "cb_profile_launches",
             "cb_profile_reset", "cb_profile_select",
             "cb_kernel_name", "cb_paged_read_probe_sink_words", "cb_paged_read_probe", "cb_sched_create", "cb_sched_add", "cb_sched_add_cached", "cb_sched_build",
             "cb_sched_commit", "cb_sched_clone", "cb_sched_destroy", "cb_sched_stats", "cb_sched_set_static",
@@ -320,6 +321,14 @@ class tuned:
         for k, v in self.saved.items():
             cb_set_tuning(k, v)
         return False
+
+
+def cb_debug_violations(reset: bool = False) -> int:
+    """Out-of-pool block ids the kernels met since the last reset (debug copy built with
+    --device-checks; raises CbError(CB_ERR_UNSUPPORTED) in the normal build)."""
+    n = ctypes.c_uint32()
+    _check(lib.cb_debug_violations(ctypes.byref(n), 1 if reset else 0))
+    return n.value
 
 
 def cb_profile_enable(on: bool) -> int:

@@ -242,6 +242,24 @@ extern "C" const char* cb_last_error(void) { return last_error().c_str(); }
 
 extern "C" const char* cb_version(void) { return "cb 0.1 gfx950"; }
 
+extern "C" int cb_debug_violations(uint32_t* count, int reset) {
+  if (!count) return fail(CB_ERR_INVALID_ARG, "cb_debug_violations: count is NULL");
+  *count = 0;
+#ifdef CB_DEVICE_CHECKS
+  if (hipDeviceSynchronize() != hipSuccess) return fail(CB_ERR_HIP, "cb_debug_violations: synchronize failed");
+  for (auto* read : {violations_rows, violations_decode_gqa, violations_prefill, violations_mixed, violations_append,
+                     violations_gemm}) {
+    const hipError_t e = read(count, reset != 0);
+    if (e != hipSuccess) return fail(CB_ERR_HIP, "cb_debug_violations: %s", hipGetErrorString(e));
+  }
+  return CB_OK;
+#else
+  (void)reset;
+  return fail(CB_ERR_UNSUPPORTED, "cb_debug_violations: this copy of the library has no device checks "
+                                  "(python -m ragged_continuous_batching_amd.build --device-checks)");
+#endif
+}
+
 namespace {
 
 // The tuning keys: name, field, and the values a key accepts (checked by cb_set_tuning;

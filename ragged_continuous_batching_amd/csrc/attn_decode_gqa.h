@@ -72,7 +72,10 @@ __device__ __forceinline__ void row_attn_mfma_waves(RowArgs a, int wg) {
 
   auto load_block = [&](int b, u32x4 (&kr)[KC], u32x2 (&vr)[DT]) {
     int blk = bt[b];
-    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = 0;
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
+      note_violation(threadIdx.x % 64 == 0);
+      blk = 0;
+    }
     const int64_t page = (static_cast<int64_t>(blk) * hkv + g) * page_elems;
     // K row `col`, dims 32*kc + 8*grp: each load reads 64 contiguous bytes of every row
     const uint16_t* kp = kbase + page + col * D + grp * 8;

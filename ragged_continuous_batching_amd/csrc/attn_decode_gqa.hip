@@ -19,4 +19,6 @@ hipError_t launch_rows_mfma(const RowArgs& a, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
+CB_VIOLATION_READER(violations_decode_gqa)
+
 }  // namespace cb

@@ -33,4 +33,6 @@ hipError_t launch_mixed(const MixedArgs& a, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
+CB_VIOLATION_READER(violations_mixed)
+
 }  // namespace cb

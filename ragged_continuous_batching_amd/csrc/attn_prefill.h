@@ -163,7 +163,11 @@ __device__ __forceinline__ void prefill_tile(PrefillArgs a, int slot) {
   // pool read block 0). The index is wave-uniform.
   const int last_page = __builtin_amdgcn_readfirstlane((wg_keys - 1) / kBlockSize);
   auto page_of = [&](int t) { return min((kt0 + t) * 4 + pw, last_page); };   // this wave's page of tile t
-  auto valid_block = [&](int blk) { return static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) ? blk : 0; };
+  auto valid_block = [&](int blk) {
+    const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+    note_violation(!ok && lane == 0);
+    return ok ? blk : 0;
+  };
   // a buffer resource over one cache page (its byte range bounds the lanes' offsets)
   auto page_rsrc = [&](const uint8_t* cache, int blk) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache + (static_cast<int64_t>(blk) * hkv + g) * PAGE),

@@ -25,4 +25,6 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int waves, hipStre
   return hipGetLastError();
 }
 
+CB_VIOLATION_READER(violations_prefill)
+
 }  // namespace cb

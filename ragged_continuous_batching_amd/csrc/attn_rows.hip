@@ -127,7 +127,10 @@ __global__ __launch_bounds__(256) void row_attn_kernel(RowArgs a) {
 
   auto load_block = [&](int b, u32x4 (&kr)[NLK], u32x4 (&vr)[NLV]) {
     int blk = bt[b];
-    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = 0;
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
+      note_violation(lane == 0);
+      blk = 0;
+    }
     const int64_t page = (static_cast<int64_t>(blk) * hkv + g) * page_elems * ES;
     // each page is read once per step: non-temporal loads keep it from displacing lines
     // that other waves still need (measured: +8% streaming read bandwidth on MI355X)
@@ -359,5 +362,7 @@ hipError_t launch_combine(const CombineArgs& a, int elem_bytes, int head_dim, hi
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+CB_VIOLATION_READER(violations_rows)
 
 }  // namespace cb

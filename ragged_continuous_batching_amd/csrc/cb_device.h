@@ -20,6 +20,34 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Buffer resource word 3 for CDNA: 32-bit data format, no swizzle, raw (stride 0) access.
 constexpr int kBufferFlags = 0x00020000;
 
+// Device checks (the debug copy of the library, built with CB_DEVICE_CHECKS). The host checks
+// a step's block ids against the pool before it launches anything, from its host mirrors; a
+// kernel reads the device block table. Where a kernel meets an id outside the pool it reads
+// block 0 instead, or skips the write, so it never faults; in the debug copy it also adds one
+// to the violation counter of its code object (every kernel source has its own counter and
+// its own reader, CB_VIOLATION_READER), which cb_debug_violations() sums. In the normal build
+// the count compiles to nothing.
+#ifdef CB_DEVICE_CHECKS
+static __device__ unsigned int g_violations;
+__device__ __forceinline__ void note_violation(bool bad) {
+  if (bad) __hip_atomic_fetch_add(&g_violations, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Host reader of this source's counter: adds it to *sum, then zeroes it when `reset`.
+#define CB_VIOLATION_READER(name)                                                              \
+  hipError_t name(uint32_t* sum, bool reset) {                                                 \
+    unsigned int v = 0;                                                                        \
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_violations), sizeof(v), 0, hipMemcpyDeviceToHost); \
+    if (e != hipSuccess) return e;                                                             \
+    *sum += v;                                                                                 \
+    if (!reset) return hipSuccess;                                                             \
+    const unsigned int zero = 0;                                                               \
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_violations), &zero, sizeof(zero), 0, hipMemcpyHostToDevice); \
+  }
+#else
+__device__ __forceinline__ void note_violation(bool) {}
+#define CB_VIOLATION_READER(name)
+#endif
+
 // bf16 stored as 16-bit patterns; a 32-bit word holds two (low half = lower address).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -88,7 +88,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bt_kernel(GemmArgs g) {
         const int p = g.ctx_lens[r] + (t - g.cu_q_lens[r]);
         blk = g.block_tables[static_cast<int64_t>(r) * g.max_blocks + p / kBlockSize];
         off = p % kBlockSize;
-        if (static_cast<unsigned>(blk) >= static_cast<unsigned>(g.num_blocks)) blk = -1;
+        if (static_cast<unsigned>(blk) >= static_cast<unsigned>(g.num_blocks)) {
+          note_violation(true);
+          blk = -1;
+        }
       }
       slot_blk[tid] = blk;
       slot_off[tid] = off;
@@ -259,5 +262,7 @@ hipError_t launch_gemm(const GemmArgs& g, int epilogue, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+CB_VIOLATION_READER(violations_gemm)
 
 }  // namespace cb

@@ -34,6 +34,17 @@ hipError_t launch_mixed(const MixedArgs& a, int head_dim, hipStream_t s);
 
 constexpr double kLog2e = 1.4426950408889634;
 
+#ifdef CB_DEVICE_CHECKS
+// The violation counters of the kernel sources (debug copy only): each adds its count to
+// *sum, and zeroes it when `reset`.
+hipError_t violations_rows(uint32_t* sum, bool reset);
+hipError_t violations_decode_gqa(uint32_t* sum, bool reset);
+hipError_t violations_prefill(uint32_t* sum, bool reset);
+hipError_t violations_mixed(uint32_t* sum, bool reset);
+hipError_t violations_append(uint32_t* sum, bool reset);
+hipError_t violations_gemm(uint32_t* sum, bool reset);
+#endif
+
 // ---- tuning -----------------------------------------------------------------------------
 struct Tuning {
   int32_t split_blocks = 0;       // 0 = automatic

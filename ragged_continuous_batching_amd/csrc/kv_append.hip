@@ -78,8 +78,10 @@ __device__ __forceinline__ void append_pages(const AppendArgs& a, int m0, int g0
     const int t = a.marked[2 * m], sl = a.marked[2 * m + 1];
     const int blk = sl / kBlockSize, off = sl % kBlockSize;
     if (sl < 0 || static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks) ||
-        static_cast<unsigned>(t) >= static_cast<unsigned>(a.num_tokens))
+        static_cast<unsigned>(t) >= static_cast<unsigned>(a.num_tokens)) {
+      note_violation(sl >= 0 && static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks));
       continue;
+    }
     at[u] = (static_cast<int64_t>(blk) * a.num_kv_heads + g0 + hh) * PCH + c;
     buf[u] = reinterpret_cast<const u32x4*>(a.v_cache)[at[u]];
     if (c % CPR == off / VEC) {
@@ -176,7 +178,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
         blk = a.block_tables[static_cast<int64_t>(r) * a.max_blocks + p / kBlockSize];
         off = p % kBlockSize;
       }
-      if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) blk = -1;
+      if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
+        note_violation(blk >= 0 || !a.slots);   // a host slot of -1 marks no row, not a bad id
+        blk = -1;
+      }
     }
     info_blk[tid] = blk;
     info_off[tid] = off;
@@ -264,5 +269,7 @@ hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int head_dim, h
   if (elem_bytes == 2) return head_dim == 128 ? launch_append_t<2, 128>(a, s) : launch_append_t<2, 64>(a, s);
   return head_dim == 128 ? launch_append_t<4, 128>(a, s) : launch_append_t<4, 64>(a, s);
 }
+
+CB_VIOLATION_READER(violations_append)
 
 }  // namespace cb

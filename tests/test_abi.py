@@ -26,6 +26,16 @@ def test_header_functions_are_exported():
     assert set(names) == set(cb.EXPORTED)
 
 
+def test_device_checks_absent_from_the_normal_build():
+    """Counting clamped block ids is a debug copy's feature; the normal library says so."""
+    if cb.LIB_PATH.endswith(os.path.join("checks", "libcb.so")):
+        pytest.skip("this process loaded the device-checks copy")
+    with pytest.raises(cb.CbError) as e:
+        cb.cb_debug_violations()
+    assert e.value.status == cb.CB_ERR_UNSUPPORTED
+    assert "--device-checks" in str(e.value)
+
+
 def test_version_and_names():
     assert "gfx950" in cb.cb_version()
     assert cb.cb_kernel_name(cb.CB_KERNEL_DECODE) == "row_attn_kernel"
